@@ -1,0 +1,347 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+P1 brute force on tiny inputs (exhaustive-ish grid, multi-step appends);
+P2 full-cache end point, P3 deepest-plane-only end point, P4 identical planes
+(all three reduce to ordinary attention: torch SDPA in fp64 on the CPU);
+P5 block independence for W >= D-1 under the query anchor (and negative
+controls); P6 loop-R rows ignore W and anchor; P7 closed forms with zero keys
+and tagged values; P8 byte layout against an independent reader and the
+brute-force dictionary; P9 the 11.9% memory figure.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.brute import BruteCache
+from oracle.memory import ripe_fraction, ripe_vectors
+from synth import WINDOW_FULL, Workload, bf16_to_f32, f32_to_bf16, grid_rows
+
+from helpers import ring_slots, split_steps, step_arrays
+from layout_ref import Image
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def tiny(lens, R, Hq, Hkv, D, W, anchor=0, seed=7, rho=0.88, heavy=0.0, d=32, n_layers=2,
+         rows=None):
+    return Workload("t", seed, n_layers, R, Hq, Hkv, d, W, D, list(lens), rho,
+                    rows if rows is not None else grid_rows(D, R), heavy_frac=heavy,
+                    anchor=anchor)
+
+
+def build_both(wl, n_steps=1, seed=0):
+    """Append the committed prefix in n_steps random pieces to the oracle and to
+    one brute-force cache per layer."""
+    cfg = oracle.config_of(wl)
+    oc = oracle.OracleCache(cfg)
+    rng = np.random.default_rng(seed)
+    steps = split_steps(wl.lens, n_steps, rng)
+    brutes = []
+    for layer in range(wl.n_layers):
+        bc = BruteCache(wl.n_loops, wl.n_heads_q, wl.n_heads_kv, wl.head_dim, wl.window,
+                        wl.batch, wl.capacity, wl.anchor)
+        L0 = [0] * wl.batch
+        for st in steps:
+            dk, dv, wk, wv = step_arrays(wl, layer, L0, st)
+            assert oc.append(layer, st, dk, dv, wk, wv) == oracle.ORA_OK
+            wr = ring_slots(wl)
+            for b in range(wl.batch):
+                n = st[b]
+                nw = min(n, wr)
+                bc.append(b, dk[b, :, :n], dv[b, :, :n], wk[b, :, :, :nw], wv[b, :, :, :nw])
+            L0 = [a + b for a, b in zip(L0, st)]
+        brutes.append(bc)
+    return oc, brutes
+
+
+def sdpa_row(q, K, V):
+    """Ordinary attention of one bf16 query over bf16 key/value rows, fp64."""
+    qf = torch.from_numpy(bf16_to_f32(q).astype(np.float64)).view(1, 1, 1, -1)
+    Kf = torch.from_numpy(bf16_to_f32(K).astype(np.float64)).view(1, 1, K.shape[0], -1)
+    Vf = torch.from_numpy(bf16_to_f32(V).astype(np.float64)).view(1, 1, V.shape[0], -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qf, Kf, Vf)
+    s = (qf @ Kf.transpose(-1, -2)) / math.sqrt(K.shape[1])
+    return o.view(-1).numpy(), torch.logsumexp(s.view(-1), 0).item()
+
+
+# ---------------------------------------------------------------- P1 + P8
+
+def _p1_cases():
+    rng = np.random.default_rng(1234)
+    cases = []
+    for L, R, D, heads in itertools.product([0, 1, 5, 11], [1, 2, 3], [1, 3, 4],
+                                            [(1, 1), (2, 1), (2, 2)]):
+        for W in sorted({0, 1, 2, 3, 5, L, L + D, WINDOW_FULL}):
+            for anchor in (0, 1):
+                cases.append((L, R, D, heads, W, anchor))
+    idx = rng.choice(len(cases), size=160, replace=False)
+    return [cases[i] for i in sorted(idx)]
+
+
+@pytest.mark.parametrize("L,R,D,heads,W,anchor", _p1_cases())
+def test_p1_brute_force_and_p8_layout(L, R, D, heads, W, anchor):
+    lens = [L, max(L - 2, 0)]
+    wl = tiny(lens, R, heads[0], heads[1], D, W, anchor=anchor, seed=L * 100 + R * 10 + D,
+              heavy=0.2)
+    oc, brutes = build_both(wl, n_steps=3, seed=L + W % 97)
+    img = Image(oc.image, wl.n_layers, R, heads[1], wl.head_dim, W, wl.batch, wl.capacity)
+    entries = []
+    for layer, bc in enumerate(brutes):
+        q = wl.queries(layer)
+        bk, bv = wl.block(layer)
+        out, lse = oc.verify(layer, wl.rows, q, bk, bv, D)
+        bout, blse = bc.verify(wl.rows, q, bk, bv)
+        np.testing.assert_allclose(out, bout, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
+        # P8: the bytes of every dictionary entry, and nothing else, are written
+        assert list(img.lens()[layer]) == bc.lens
+        for (b, g, p, plane), (k, v) in bc.store.items():
+            got = img.deep(layer, b, g, p) if plane == R else img.ring(layer, b, g, plane, p)
+            assert np.array_equal(got[0], k) and np.array_equal(got[1], v), (b, g, p, plane)
+            entries.append((layer, b, g, p, plane))
+        # live entries per (sequence, head): L + min(W, L) * (R - 1)
+        for b in range(wl.batch):
+            for g in range(heads[1]):
+                assert bc.entries(b, g) == ripe_vectors(bc.lens[b], min(W, wl.capacity), R, 1)
+    mask = img.written_mask(entries)
+    assert not np.any(oc.image[~mask]), "bytes written outside the stored entries"
+
+
+# ---------------------------------------------------------------- P2 P3 P4 P6
+
+def _keys_for(wl, layer, b, i, r, plane_rule):
+    """Logical keys/values of one row, built from the generator directly.
+    plane_rule(s) -> plane for committed position s."""
+    L = wl.lens[b]
+    g_all = range(wl.n_heads_kv)
+    K = np.zeros((wl.n_heads_kv, L + i + 1, wl.head_dim), np.uint16)
+    V = np.zeros_like(K)
+    for s in range(L):
+        k, v = wl.planes(layer, b, s, s + 1, [plane_rule(s)])
+        K[:, s] = k[0, :, 0]
+        V[:, s] = v[0, :, 0]
+    k, v = wl.planes(layer, b, L, L + i + 1, [r])
+    K[:, L:] = k[0]
+    V[:, L:] = v[0]
+    del g_all
+    return K, V
+
+
+def _check_rows_against(wl, oc, rule_for_row, layers=(0,)):
+    grp = wl.n_heads_q // wl.n_heads_kv
+    for layer in layers:
+        q = wl.queries(layer)
+        bk, bv = wl.block(layer)
+        out, lse = oc.verify(layer, wl.rows, q, bk, bv, wl.n_blk)
+        for b in range(wl.batch):
+            for kk, (i, r) in enumerate(wl.rows):
+                K, V = _keys_for(wl, layer, b, i, r, rule_for_row(b, i, r))
+                for h in range(wl.n_heads_q):
+                    o, l = sdpa_row(q[b, kk, h], K[h // grp], V[h // grp])
+                    np.testing.assert_allclose(out[b, kk, h], o, rtol=0, atol=1e-10)
+                    assert abs(lse[b, kk, h] - l) < 1e-10
+
+
+@pytest.mark.parametrize("anchor,W", [(1, 23), (1, WINDOW_FULL), (0, 23 + 4 - 1), (0, WINDOW_FULL)])
+def test_p2_full_cache_endpoint(anchor, W):
+    wl = tiny([23, 17], 4, 2, 1, 4, W, anchor=anchor, heavy=0.1)
+    oc, _ = build_both(wl, n_steps=2)
+    _check_rows_against(wl, oc, lambda b, i, r: (lambda s: r))
+
+
+@pytest.mark.parametrize("anchor", [0, 1])
+def test_p3_deepest_plane_endpoint(anchor):
+    wl = tiny([20, 9], 4, 4, 2, 3, 0, anchor=anchor, heavy=0.1)
+    oc, _ = build_both(wl, n_steps=2)
+    R = wl.n_loops
+    _check_rows_against(wl, oc, lambda b, i, r: (lambda s: R))
+
+
+@pytest.mark.parametrize("anchor,W", [(0, 0), (0, 5), (1, 5), (1, 40), (0, WINDOW_FULL)])
+def test_p4_identical_planes_reduce_to_causal_attention(anchor, W):
+    wl = tiny([19, 6], 3, 2, 2, 4, W, anchor=anchor, rho=0.0)
+    oc, _ = build_both(wl, n_steps=2)
+    R = wl.n_loops
+    _check_rows_against(wl, oc, lambda b, i, r: (lambda s: R))
+
+
+def test_p6_loop_R_rows_ignore_window_and_anchor():
+    base = None
+    for W, anchor in [(0, 0), (3, 0), (3, 1), (10, 1), (WINDOW_FULL, 0)]:
+        wl = tiny([15, 12], 3, 2, 1, 3, W, anchor=anchor, rows=[(i, 3) for i in range(3)])
+        oc, _ = build_both(wl, n_steps=2)
+        q = wl.queries(0)
+        bk, bv = wl.block(0)
+        out, lse = oc.verify(0, wl.rows, q, bk, bv, 3)
+        if base is None:
+            base = (out, lse)
+        else:
+            assert np.array_equal(out, base[0]) and np.array_equal(lse, base[1])
+
+
+# ---------------------------------------------------------------- P5
+
+def _split_equivalence(W, anchor, D=4, k=2, L=13):
+    """One D-row call vs rows i<k at length L, append k tokens, rows i>=k."""
+    R = 3
+    wl = tiny([L], R, 2, 1, D, W, anchor=anchor, heavy=0.0, n_layers=1)
+    rows = grid_rows(D, R)
+    oc, _ = build_both(wl, n_steps=1)
+    q = wl.queries(0)
+    wl_rows = wl.replace(rows=rows)
+    q = wl_rows.queries(0)
+    bk, bv = wl.block(0)
+    full_out, full_lse = oc.verify(0, rows, q, bk, bv, D)
+    # split: first the rows with i < k at length L
+    first = [(i, r) for (i, r) in rows if i < k]
+    idx_first = [rows.index(x) for x in first]
+    o1, l1 = oc.verify(0, first, q[:, idx_first], bk, bv, D)
+    # append the first k block tokens (plane R plus the window planes)
+    dk, dv, wk, wv = step_arrays(wl, 0, [L], [k])
+    assert oc.append(0, [k], dk, dv, wk, wv) == oracle.ORA_OK
+    second = [(i - k, r) for (i, r) in rows if i >= k]
+    idx_second = [rows.index((i + k, r)) for (i, r) in second]
+    bk2 = np.zeros_like(bk)
+    bv2 = np.zeros_like(bv)
+    bk2[:, :, :, :D - k] = bk[:, :, :, k:D]
+    bv2[:, :, :, :D - k] = bv[:, :, :, k:D]
+    o2, l2 = oc.verify(0, second, q[:, idx_second], bk2, bv2, D - k)
+    split_out = np.zeros_like(full_out)
+    split_lse = np.zeros_like(full_lse)
+    split_out[:, idx_first], split_lse[:, idx_first] = o1, l1
+    split_out[:, idx_second], split_lse[:, idx_second] = o2, l2
+    return (np.array_equal(full_out, split_out) and np.array_equal(full_lse, split_lse),
+            np.max(np.abs(full_out - split_out)))
+
+
+@pytest.mark.parametrize("W", [3, 4, 6, 20])
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_p5_block_independence_query_anchor(W, k):
+    same, _ = _split_equivalence(W, 0, D=4, k=k)
+    assert same
+
+
+@pytest.mark.parametrize("W,anchor,k", [(2, 0, 1), (1, 0, 2), (3, 1, 1), (6, 1, 2)])
+def test_p5_negative_controls(W, anchor, k):
+    same, diff = _split_equivalence(W, anchor, D=4, k=k)
+    assert not same and diff > 1e-6
+
+
+# ---------------------------------------------------------------- P7
+
+def _tagged_cache(L, R, W, anchor, D):
+    """A cache whose keys are all zero and whose values tag (plane, position)."""
+    H, d = 1, 32
+    cfg = oracle.config(1, R, 1, H, d, W, 1, L + D, D, anchor)
+    oc = oracle.OracleCache(cfg)
+    wr = 0 if R == 1 else min(W, L + D)
+    zero = f32_to_bf16(np.zeros(1, np.float32))[0]
+
+    def val(p, r):
+        v = np.zeros(d, np.float32)
+        v[0] = r
+        v[1] = p
+        v[2] = 1.0
+        return f32_to_bf16(v)
+
+    dk = np.full((1, H, max(L, 1), d), zero, np.uint16)
+    dv = np.zeros((1, H, max(L, 1), d), np.uint16)
+    for p in range(L):
+        dv[0, 0, p] = val(p, R)
+    nw = min(L, wr)
+    wk = np.full((1, max(R - 1, 1), H, max(nw, 1), d), zero, np.uint16)
+    wv = np.zeros((1, max(R - 1, 1), H, max(nw, 1), d), np.uint16)
+    for u in range(nw):
+        p = L - nw + u
+        for r in range(1, R):
+            wv[0, r - 1, 0, u] = val(p, r)
+    assert oc.append(0, [L], dk, dv, wk, wv) == oracle.ORA_OK
+    bk = np.full((1, R, H, D, d), zero, np.uint16)
+    bv = np.zeros((1, R, H, D, d), np.uint16)
+    for r in range(1, R + 1):
+        for j in range(D):
+            bv[0, r - 1, 0, j] = val(L + j, r)
+    return oc, bk, bv
+
+
+@pytest.mark.parametrize("L,R,W,anchor,D", [(12, 4, 5, 0, 3), (12, 4, 5, 1, 3), (7, 3, 0, 0, 4),
+                                            (9, 5, 20, 0, 2), (30, 6, 8, 0, 5), (30, 6, 8, 1, 5)])
+def test_p7_uniform_softmax_closed_form(L, R, W, anchor, D):
+    oc, bk, bv = _tagged_cache(L, R, W, anchor, D)
+    rows = grid_rows(D, R)
+    q = f32_to_bf16(np.random.default_rng(3).standard_normal((1, len(rows), 1, 32)).astype(np.float32))
+    out, lse = oc.verify(0, rows, q, bk, bv, D)
+    for kk, (i, r) in enumerate(rows):
+        t = L + i
+        n = t + 1
+        beta = t - W if anchor == 0 else L - W
+        n_deep = min(max(beta, 0), L)          # committed keys read at loop R
+        mean_plane = (R * n_deep + r * (n - n_deep)) / n
+        assert abs(lse[0, kk, 0] - math.log(n)) < 1e-12
+        assert abs(out[0, kk, 0, 0] - mean_plane) < 1e-12
+        assert abs(out[0, kk, 0, 1] - t / 2.0) < 1e-12
+        assert abs(out[0, kk, 0, 2] - 1.0) < 1e-12
+
+
+def test_p7_single_key():
+    """L = 0 and block offset 0: one key, O = v and LSE = score."""
+    wl = tiny([0], 2, 1, 1, 1, 4, n_layers=1)
+    oc, _ = build_both(wl)
+    q = wl.queries(0)
+    bk, bv = wl.block(0)
+    out, lse = oc.verify(0, wl.rows, q, bk, bv, 1)
+    for kk, (i, r) in enumerate(wl.rows):
+        k = bf16_to_f32(bk[0, r - 1, 0, 0]).astype(np.float64)
+        v = bf16_to_f32(bv[0, r - 1, 0, 0]).astype(np.float64)
+        qq = bf16_to_f32(q[0, kk, 0]).astype(np.float64)
+        assert abs(lse[0, kk, 0] - qq @ k / math.sqrt(32)) < 1e-12
+        np.testing.assert_array_equal(out[0, kk, 0], v)
+
+
+# ---------------------------------------------------------------- P9 and errors
+
+def _golden(name):
+    vals = {}
+    for line in open(os.path.join(HERE, "golden", name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split()
+            vals[k] = float(v)
+    return vals
+
+
+def test_p9_memory_fraction_matches_page():
+    g = _golden("memory_fraction.txt")
+    # Assumption (not on the pages): Huginn-scale model with 4 recurrent layers
+    # at R = 32 loops and 4 single-plane layers outside the recurrence.
+    f = ripe_fraction(int(g["context"]), int(g["window"]), 32, n_recurrent=4, n_plain=4)
+    assert abs(100 * f - g["fraction_percent"]) <= g["print_precision_percent"]
+    # the stored vectors of the byte layout agree with the closed form
+    wl = tiny([40], 5, 1, 1, 1, 7, n_layers=1)
+    oc, brutes = build_both(wl, n_steps=3)
+    assert brutes[0].entries(0, 0) == ripe_vectors(40, 7, 5, 1)
+
+
+def test_capacity_error_leaves_state_unchanged():
+    wl = tiny([10], 3, 1, 1, 2, 4, n_layers=1)
+    oc, _ = build_both(wl)
+    before = oc.image.copy()
+    dk, dv, wk, wv = step_arrays(wl, 0, [10], [wl.capacity])
+    assert oc.append(0, [wl.capacity], dk, dv, wk, wv) == oracle.ORA_ECAPACITY
+    assert np.array_equal(before, oc.image)
+
+
+def test_invalid_rows_rejected():
+    wl = tiny([10], 3, 1, 1, 2, 4, n_layers=1)
+    oc, _ = build_both(wl)
+    q = wl.queries(0)
+    bk, bv = wl.block(0)
+    with pytest.raises(RuntimeError):
+        oc.verify(0, [(2, 1)] * wl.n_rows, q, bk, bv, 2)   # block offset >= n_blk
+    with pytest.raises(RuntimeError):
+        oc.verify(0, [(0, 4)] * wl.n_rows, q, bk, bv, 2)   # loop > R
