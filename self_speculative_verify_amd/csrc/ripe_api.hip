@@ -1,0 +1,273 @@
+// Host side of the RIPE C ABI: configuration checks, storage geometry, the
+// host copy of the committed lengths, and kernel launches on the caller's
+// stream.  See include/ripe.h for the contract of every entry point.
+#include "ripe.h"
+#include "ripe_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+using ripe::Geometry;
+
+struct ripe_cache {
+    uint64_t magic;
+    Geometry g;
+    uint8_t* storage;
+    std::vector<int32_t> lens;   // [n_layers][B], host copy of the lens section
+};
+
+namespace {
+
+constexpr uint64_t kMagic = 0x52495045434143ull;   // "RIPECAC"
+
+int64_t up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool valid_config(const ripe_config* c) {
+    if (!c) return false;
+    if (c->n_layers < 1 || c->n_loops < 1 || c->n_loops > 255) return false;
+    if (c->n_heads_kv < 1 || c->n_heads_q < 1 || c->n_heads_q % c->n_heads_kv) return false;
+    if (c->head_dim != 64 && c->head_dim != 96 && c->head_dim != 128) return false;
+    if (c->window < 0 || c->batch < 1 || c->batch > 4096) return false;
+    if (c->capacity < 1 || c->max_block < 1 || c->max_block > 256) return false;
+    if (c->anchor != RIPE_ANCHOR_QUERY && c->anchor != RIPE_ANCHOR_CACHE) return false;
+    // element counts must stay far from int64 overflow
+    const double elems = (double)c->n_layers * c->batch * c->n_heads_kv * c->head_dim *
+                         ((double)c->capacity + 32.0) * c->n_loops;
+    return elems < 4.0e15;
+}
+
+Geometry geometry(const ripe_config* c) {
+    Geometry g;
+    g.n_layers = c->n_layers; g.R = c->n_loops; g.Hq = c->n_heads_q; g.Hkv = c->n_heads_kv;
+    g.d = c->head_dim; g.W = c->window; g.B = c->batch; g.cap = c->capacity;
+    g.max_block = c->max_block; g.anchor = c->anchor;
+    g.CP = up(c->capacity, ripe::kTile);
+    g.NR = c->n_loops - 1;
+    g.WR = g.NR == 0 ? 0 : std::min<int64_t>(c->window, c->capacity);
+    g.WP = up(g.WR, ripe::kTile);
+    const int64_t NL = g.n_layers, B = g.B, H = g.Hkv, d = g.d;
+    int64_t off = 0;
+    g.off_lens = off;   off = up(off + NL * B * 4, 256);
+    g.off_deep_k = off; off = up(off + NL * B * H * g.CP * d * 2, 256);
+    g.off_deep_v = off; off = up(off + NL * B * H * g.CP * d * 2, 256);
+    g.off_ring_k = off; off = up(off + NL * B * H * g.NR * g.WP * d * 2, 256);
+    g.off_ring_v = off; off = up(off + NL * B * H * g.NR * g.WP * d * 2, 256);
+    g.total = off;
+    return g;
+}
+
+bool live(const ripe_cache* c) { return c && c->magic == kMagic; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// a view is usable for vectors of d elements: 16-byte aligned pointer, strides
+// non-negative multiples of 8 elements
+bool view_ok(const ripe_kv_view& v) {
+    if (!v.ptr || !aligned(v.ptr, 16)) return false;
+    const int64_t s[4] = {v.s_b, v.s_plane, v.s_head, v.s_tok};
+    for (int64_t x : s)
+        if (x < 0 || x % 8) return false;
+    return true;
+}
+
+ripe::View as_view(const ripe_kv_view& v) {
+    return ripe::View{static_cast<const uint16_t*>(v.ptr), v.s_b, v.s_plane, v.s_head, v.s_tok};
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ripe_cache_bytes(const ripe_config* cfg) {
+    if (!valid_config(cfg)) return 0;
+    return (size_t)geometry(cfg).total;
+}
+
+int64_t ripe_section_offset(const ripe_config* cfg, int32_t section) {
+    if (!valid_config(cfg)) return -1;
+    const Geometry g = geometry(cfg);
+    switch (section) {
+        case RIPE_SECTION_LENS: return g.off_lens;
+        case RIPE_SECTION_DEEP_K: return g.off_deep_k;
+        case RIPE_SECTION_DEEP_V: return g.off_deep_v;
+        case RIPE_SECTION_RING_K: return g.off_ring_k;
+        case RIPE_SECTION_RING_V: return g.off_ring_v;
+        case RIPE_SECTION_END: return g.total;
+    }
+    return -1;
+}
+
+ripe_status ripe_cache_create(const ripe_config* cfg, void* d_storage, size_t bytes,
+                              hipStream_t stream, ripe_cache** out) {
+    if (!out) return RIPE_EINVAL;
+    *out = nullptr;
+    if (!valid_config(cfg) || !d_storage || !aligned(d_storage, 256)) return RIPE_EINVAL;
+    const Geometry g = geometry(cfg);
+    if (bytes < (size_t)g.total) return RIPE_EINVAL;
+    ripe_cache* c = new (std::nothrow) ripe_cache;
+    if (!c) return RIPE_EDEVICE;
+    c->magic = kMagic;
+    c->g = g;
+    c->storage = static_cast<uint8_t*>(d_storage);
+    c->lens.assign((size_t)g.n_layers * g.B, 0);
+    if (hipMemsetAsync(d_storage, 0, (size_t)g.total, stream) != hipSuccess) {
+        c->magic = 0;
+        delete c;
+        return RIPE_EDEVICE;
+    }
+    *out = c;
+    return RIPE_OK;
+}
+
+void ripe_destroy(ripe_cache* cache) {
+    if (!live(cache)) return;
+    cache->magic = 0;
+    delete cache;
+}
+
+ripe_status ripe_get_lengths(const ripe_cache* cache, int32_t layer, int32_t* h_lens) {
+    if (!live(cache) || !h_lens || layer < 0 || layer >= cache->g.n_layers) return RIPE_EINVAL;
+    std::memcpy(h_lens, cache->lens.data() + (size_t)layer * cache->g.B, sizeof(int32_t) * cache->g.B);
+    return RIPE_OK;
+}
+
+ripe_status ripe_append(ripe_cache* cache, int32_t layer, const int32_t* h_n_new,
+                        ripe_kv_view deep_k, ripe_kv_view deep_v, ripe_kv_view win_k,
+                        ripe_kv_view win_v, hipStream_t stream) {
+    if (!live(cache) || !h_n_new || layer < 0 || layer >= cache->g.n_layers) return RIPE_EINVAL;
+    const Geometry& g = cache->g;
+    int32_t* lens = cache->lens.data() + (size_t)layer * g.B;
+    int64_t n_tok = 0, n_win = 0;
+    for (int b = 0; b < g.B; ++b) {
+        if (h_n_new[b] < 0) return RIPE_EINVAL;
+        n_tok += h_n_new[b];
+        n_win += std::min<int64_t>(h_n_new[b], g.WR);
+    }
+    for (int b = 0; b < g.B; ++b)
+        if ((int64_t)lens[b] + h_n_new[b] > g.cap) return RIPE_ECAPACITY;
+    if (n_tok == 0) return RIPE_OK;
+    if (!view_ok(deep_k) || !view_ok(deep_v)) return RIPE_EINVAL;
+    if (n_win > 0 && (!view_ok(win_k) || !view_ok(win_v))) return RIPE_EINVAL;
+
+    ripe::AppendArgs a;
+    std::memset(&a, 0, sizeof(a));
+    const int64_t lk = (int64_t)layer * g.B * g.Hkv;
+    a.deep_k = reinterpret_cast<uint16_t*>(cache->storage + g.off_deep_k) + lk * g.CP * g.d;
+    a.deep_v = reinterpret_cast<uint16_t*>(cache->storage + g.off_deep_v) + lk * g.CP * g.d;
+    a.ring_k = reinterpret_cast<uint16_t*>(cache->storage + g.off_ring_k) + lk * g.NR * g.WP * g.d;
+    a.ring_v = reinterpret_cast<uint16_t*>(cache->storage + g.off_ring_v) + lk * g.NR * g.WP * g.d;
+    a.lens = reinterpret_cast<int32_t*>(cache->storage + g.off_lens) + (int64_t)layer * g.B;
+    a.dk = as_view(deep_k);
+    a.dv = as_view(deep_v);
+    if (n_win > 0) {
+        a.wk = as_view(win_k);
+        a.wv = as_view(win_v);
+    }
+    a.Hkv = g.Hkv; a.d = g.d; a.NR = (int32_t)g.NR;
+    a.CP = g.CP; a.WR = g.WR; a.WP = g.WP;
+    const int64_t per_tok = (int64_t)g.Hkv * (g.d / 8);
+    for (int b0 = 0; b0 < g.B; b0 += ripe::kMaxBatchPerLaunch) {
+        a.b0 = b0;
+        a.nb = std::min(ripe::kMaxBatchPerLaunch, g.B - b0);
+        int64_t pd = 0;
+        bool any = false;
+        for (int s = 0; s < a.nb; ++s) {
+            a.n_new[s] = h_n_new[b0 + s];
+            a.L0[s] = lens[b0 + s];
+            a.n_win[s] = (int32_t)std::min<int64_t>(a.n_new[s], g.WR);
+            a.prefix[s] = pd;
+            pd += (int64_t)a.n_new[s] * per_tok;
+            any = any || a.n_new[s] > 0;
+        }
+        a.prefix[a.nb] = pd;
+        if (!any) continue;
+        a.total = pd;
+        if (ripe::launch_append_deep(a, stream) != hipSuccess) return RIPE_EDEVICE;
+        if (g.NR > 0 && g.WR > 0) {
+            int64_t pr = 0;
+            for (int s = 0; s < a.nb; ++s) {
+                a.prefix[s] = pr;
+                pr += (int64_t)a.n_win[s] * g.NR * per_tok;
+            }
+            a.prefix[a.nb] = pr;
+            a.total = pr;
+            if (pr > 0 && ripe::launch_append_ring(a, stream) != hipSuccess) return RIPE_EDEVICE;
+        }
+    }
+    for (int b = 0; b < g.B; ++b) lens[b] += h_n_new[b];
+    return RIPE_OK;
+}
+
+size_t ripe_workspace_bytes(const ripe_cache* cache, int32_t n_rows) {
+    if (!live(cache) || n_rows < 0) return 0;
+    return 0;
+}
+
+ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
+                             const int32_t* h_row_blk, const int32_t* h_row_loop,
+                             const void* d_q, ripe_kv_view blk_k, ripe_kv_view blk_v,
+                             int32_t n_blk, float* d_out, float* d_lse, void* d_ws,
+                             size_t ws_bytes, hipStream_t stream) {
+    if (!live(cache) || layer < 0 || layer >= cache->g.n_layers) return RIPE_EINVAL;
+    const Geometry& g = cache->g;
+    if (n_rows < 0 || n_rows > 65535) return RIPE_EINVAL;
+    if (n_rows == 0) return RIPE_OK;
+    if (!h_row_blk || !h_row_loop || !d_q || !d_out || !d_lse) return RIPE_EINVAL;
+    if (n_blk < 1 || n_blk > g.max_block) return RIPE_EINVAL;
+    if (!aligned(d_q, 16) || !aligned(d_out, 16) || !aligned(d_lse, 4)) return RIPE_EINVAL;
+    if (!view_ok(blk_k) || !view_ok(blk_v)) return RIPE_EINVAL;
+    for (int k = 0; k < n_rows; ++k) {
+        if (h_row_blk[k] < 0 || h_row_blk[k] >= n_blk) return RIPE_EINVAL;
+        if (h_row_loop[k] < 1 || h_row_loop[k] > g.R) return RIPE_EINVAL;
+    }
+    const size_t need = ripe_workspace_bytes(cache, n_rows);
+    if (ws_bytes < need || (need > 0 && (!d_ws || !aligned(d_ws, 256)))) return RIPE_EINVAL;
+
+    // rows sorted by (loop, block offset) so that rows reading the same planes
+    // are adjacent
+    std::vector<uint32_t> rows((size_t)n_rows);
+    for (int k = 0; k < n_rows; ++k)
+        rows[k] = (uint32_t)h_row_blk[k] | ((uint32_t)h_row_loop[k] << 8) | ((uint32_t)k << 16);
+    std::stable_sort(rows.begin(), rows.end(),
+                     [](uint32_t x, uint32_t y) { return (x & 0xffffu) < (y & 0xffffu); });
+
+    ripe::VerifyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    const int64_t lk = (int64_t)layer * g.B * g.Hkv;
+    a.deep_k = reinterpret_cast<const uint16_t*>(cache->storage + g.off_deep_k) + lk * g.CP * g.d;
+    a.deep_v = reinterpret_cast<const uint16_t*>(cache->storage + g.off_deep_v) + lk * g.CP * g.d;
+    a.ring_k = reinterpret_cast<const uint16_t*>(cache->storage + g.off_ring_k) + lk * g.NR * g.WP * g.d;
+    a.ring_v = reinterpret_cast<const uint16_t*>(cache->storage + g.off_ring_v) + lk * g.NR * g.WP * g.d;
+    a.lens = reinterpret_cast<const int32_t*>(cache->storage + g.off_lens) + (int64_t)layer * g.B;
+    a.q = static_cast<const uint16_t*>(d_q);
+    a.bk = as_view(blk_k);
+    a.bv = as_view(blk_v);
+    a.out = d_out;
+    a.lse = d_lse;
+    a.part = static_cast<float*>(d_ws);
+    a.B = g.B; a.n_rows = n_rows; a.Hq = g.Hq; a.Hkv = g.Hkv; a.group = g.Hq / g.Hkv;
+    a.R = g.R; a.d = g.d; a.n_blk = n_blk; a.anchor = g.anchor;
+    a.W = g.W; a.CP = g.CP; a.WR = g.WR; a.WP = g.WP; a.NR = g.NR;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
+    for (int k0 = 0; k0 < n_rows; k0 += ripe::kMaxRowsPerLaunch) {
+        a.rows_here = std::min(ripe::kMaxRowsPerLaunch, n_rows - k0);
+        for (int k = 0; k < a.rows_here; ++k) a.rows[k] = rows[k0 + k];
+        if (ripe::launch_verify_valu(a, stream) != hipSuccess) return RIPE_EDEVICE;
+    }
+    return RIPE_OK;
+}
+
+const char* ripe_status_string(ripe_status s) {
+    switch (s) {
+        case RIPE_OK: return "ok";
+        case RIPE_EINVAL: return "invalid argument";
+        case RIPE_ECAPACITY: return "append exceeds capacity";
+        case RIPE_EDEVICE: return "HIP launch or runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

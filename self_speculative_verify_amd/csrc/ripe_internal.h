@@ -1,0 +1,91 @@
+// Internal declarations shared by the host side of the library and its HIP
+// kernels (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ripe {
+
+constexpr int kTile = 32;          // rows (positions or ring slots) per tile
+constexpr int kMaxBatchPerLaunch = 64;
+constexpr int kMaxRowsPerLaunch = 256;
+
+// Storage geometry derived from a configuration (all counts, no bytes).
+struct Geometry {
+    int32_t n_layers, R, Hq, Hkv, d, W, B, cap, max_block, anchor;
+    int64_t CP;   // deep rows per (layer, seq, head), multiple of 32
+    int64_t WR;   // ring slots in use
+    int64_t WP;   // ring rows allocated, multiple of 32
+    int64_t NR;   // ring planes (R - 1)
+    int64_t off_lens, off_deep_k, off_deep_v, off_ring_k, off_ring_v, total;
+};
+
+// Element offset of (row, dim) inside one tile region, keys and values.
+__host__ __device__ inline int64_t key_off(int64_t row, int e, int d) {
+    return (row >> 5) * (int64_t)(kTile * d) + (e >> 5) * 1024 + (row & 31) * 32 + (e & 31);
+}
+// Column of row k (0..31) of a 32-row value tile.  With this order, the two
+// 16-row halves of a score tile computed by v_mfma_f32_16x16x32_bf16 (lane
+// group q holding rows 4q..4q+3 of each half) feed the value operand of the
+// same instruction as 8 consecutive columns 8q..8q+7.
+__host__ __device__ inline int v_slot(int k) {
+    return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
+}
+__host__ __device__ inline int64_t val_off(int64_t row, int e, int d) {
+    return (row >> 5) * (int64_t)(kTile * d) + (int64_t)e * 32 + v_slot((int)(row & 31));
+}
+
+struct View {            // strided bf16 view, element strides
+    const uint16_t* p;
+    int64_t sb, sp, sh, st;
+};
+
+// ---------------------------------------------------------------- append
+
+struct AppendArgs {
+    uint16_t* deep_k;    // layer base of the deep sections: [B][Hkv][CP*d]
+    uint16_t* deep_v;
+    uint16_t* ring_k;    // layer base of the ring sections: [B][Hkv][NR][WP*d]
+    uint16_t* ring_v;
+    int32_t* lens;       // layer row of the lens section: [B]
+    View dk, dv, wk, wv;
+    int32_t Hkv, d, NR;
+    int64_t CP, WR, WP;
+    int32_t nb;          // sequences in this launch
+    int32_t b0;          // first sequence
+    int64_t total;       // work items of this launch
+    int32_t n_new[kMaxBatchPerLaunch];
+    int32_t L0[kMaxBatchPerLaunch];
+    int32_t n_win[kMaxBatchPerLaunch];
+    int64_t prefix[kMaxBatchPerLaunch + 1];   // per-sequence work-item prefix
+};
+
+hipError_t launch_append_deep(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_ring(const AppendArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- verify
+
+struct VerifyArgs {
+    const uint16_t* deep_k;  // layer base: [B][Hkv][CP*d]
+    const uint16_t* deep_v;
+    const uint16_t* ring_k;  // layer base: [B][Hkv][NR][WP*d]
+    const uint16_t* ring_v;
+    const int32_t* lens;     // layer row of the lens section
+    const uint16_t* q;       // [B][n_rows][Hq][d]
+    View bk, bv;             // draft block planes
+    float* out;              // [B][n_rows][Hq][d]
+    float* lse;              // [B][n_rows][Hq]
+    float* part;             // partial softmax states (split key ranges)
+    int32_t B, n_rows, Hq, Hkv, group, R, d, n_blk, anchor;
+    int64_t W, CP, WR, WP, NR;
+    float scale_log2;        // log2(e) / sqrt(d)
+    int32_t rows_here;       // rows in this launch
+    // rows of this launch sorted by (loop, block offset):
+    // bits 0..7 block offset, 8..15 loop, 16..31 row index in the call
+    uint32_t rows[kMaxRowsPerLaunch];
+};
+
+hipError_t launch_verify_valu(const VerifyArgs& a, hipStream_t s);
+
+}  // namespace ripe

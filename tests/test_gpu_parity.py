@@ -1,0 +1,213 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Layout: storage bytes bit-exact against the oracle's image after prefix
+appends and after block appends that evict positions from the window.
+Attention: max |O - O_ref| <= 2e-3 and |LSE - LSE_ref| / max(1, |LSE_ref|)
+<= 1e-5 on every output, for reduced versions of the five workloads (sizes
+the oracle finishes in seconds) and edge cases; the tagged-value probe checks
+the exact key set of every row.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import WINDOW_FULL, Workload, f32_to_bf16, grid_rows, named_workload, wave_rows
+
+from helpers import step_arrays
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 2e-3
+TOL_LSE = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import self_speculative_verify_amd.ripe as r
+    r.load()   # raises if the HIP library is not built
+    yield
+
+
+def _h():
+    import ripe_harness
+    return ripe_harness
+
+
+def assert_close(out, lse, ref_out, ref_lse, what=""):
+    o = out.detach().cpu().double().numpy()
+    l = lse.detach().cpu().double().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), what
+    err_o = float(np.max(np.abs(o - ref_out))) if o.size else 0.0
+    err_l = float(np.max(np.abs(l - ref_lse) / np.maximum(1.0, np.abs(ref_lse)))) if l.size else 0.0
+    print(f"{what}: max|dO|={err_o:.3e} max rel dLSE={err_l:.3e}", flush=True)
+    assert err_o <= TOL_O, f"{what}: max |dO| = {err_o}"
+    assert err_l <= TOL_LSE, f"{what}: max rel dLSE = {err_l}"
+
+
+def run_case(wl: Workload, window=None, anchor=None, layers=(0,), rows=None):
+    H = _h()
+    window = wl.window if window is None else window
+    anchor = wl.anchor if anchor is None else anchor
+    cache = H.make_cache(wl, window=window, anchor=anchor)
+    H.load_prefix(cache, wl, layers)
+    oc = oracle.prefix_cache(wl, layers=layers, anchor=anchor, window=window)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.storage.cpu().numpy(), oc.image), "layout differs from the oracle"
+    rows = wl.rows if rows is None else rows
+    wl_r = wl.replace(rows=list(rows))
+    for layer in layers:
+        q, bk, bv = H.verify_inputs(wl_r, layer)
+        out, lse = cache.verify(layer, rows, q, bk, bv, wl.n_blk)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oc.verify(layer, rows, wl_r.queries(layer), *wl_r.block(layer), wl.n_blk)
+        assert_close(out, lse, ref_o, ref_l, f"{wl.name} W={window} anchor={anchor} layer={layer}")
+    return cache, oc
+
+
+# ---------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("window", [16, WINDOW_FULL])
+@pytest.mark.parametrize("anchor", [0, 1])
+def test_tiny_both_layouts(window, anchor):
+    run_case(named_workload("tiny"), window=window, anchor=anchor)
+
+
+@pytest.mark.parametrize("window", [0, 8, 64, 1024])
+def test_huginn_one_layer(window):
+    wl = named_workload("huginn", n_layers=1, n_heads_q=11, n_heads_kv=11)
+    run_case(wl, window=window)
+
+
+@pytest.mark.parametrize("window,anchor", [(0, 0), (WINDOW_FULL, 0), (1024, 0), (1024, 1)])
+def test_gqa_reduced(window, anchor):
+    wl = named_workload("gqa", n_layers=1, lens=[1024, 1024])
+    run_case(wl, window=window, anchor=anchor)
+
+
+def test_ragged_reduced_with_block_append():
+    wl = named_workload("ragged", n_layers=1, lens=[1500, 33, 700, 2100])
+    cache, oc = run_case(wl)
+    # accept the whole draft block: append its D tokens (loop R to the deep rows,
+    # loops 1..R-1 to the ring, evicting the oldest window positions)
+    H = _h()
+    bk, bv = wl.block(0)
+    D = wl.n_blk
+    R = wl.n_loops
+    tbk, tbv = H.to_dev(bk), H.to_dev(bv)
+    cache.append(0, [D] * wl.batch, tbk[:, R - 1, :, :D], tbv[:, R - 1, :, :D],
+                 tbk[:, :R - 1, :, :D], tbv[:, :R - 1, :, :D])
+    deep_k = np.ascontiguousarray(bk[:, R - 1, :, :D])
+    deep_v = np.ascontiguousarray(bv[:, R - 1, :, :D])
+    assert oc.append(0, [D] * wl.batch, deep_k, deep_v, bk[:, :R - 1, :, :D],
+                     bv[:, :R - 1, :, :D]) == oracle.ORA_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.storage.cpu().numpy(), oc.image), "layout after block append"
+    assert cache.lengths(0) == [L + D for L in wl.lens]
+    # verify the next block at the new lengths
+    wl2 = wl.replace(lens=[L + D for L in wl.lens], capacity=wl.capacity)
+    q, bk2, bv2 = H.verify_inputs(wl2, 0)
+    out, lse = cache.verify(0, wl2.rows, q, bk2, bv2, D)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oc.verify(0, wl2.rows, wl2.queries(0), *wl2.block(0), D)
+    assert_close(out, lse, ref_o, ref_l, "ragged after append")
+
+
+def test_wave_reduced():
+    wl = named_workload("wave", n_layers=1, lens=[2048], n_heads_q=11, n_heads_kv=11)
+    run_case(wl)
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("lens,window,anchor", [
+    ([0, 5, 37], 4, 0),          # empty and short sequences
+    ([31, 32, 33], 40, 0),       # window longer than the context
+    ([64, 3, 100], 7, 1),
+    ([90, 90, 1], WINDOW_FULL, 1),
+])
+def test_edge_lengths(lens, window, anchor):
+    wl = Workload("edge", 77, 1, 5, 4, 2, 64, window, 3, lens, 0.88, grid_rows(3, 5),
+                  heavy_frac=0.05, max_block=5)
+    run_case(wl, window=window, anchor=anchor)
+
+
+def test_row_subset_any_order_with_repeats():
+    wl = Workload("rows", 78, 1, 6, 4, 1, 128, 9, 5, [200, 50], 0.81, grid_rows(5, 6))
+    rows = [(4, 2), (0, 6), (4, 2), (2, 1), (3, 6), (1, 3), (0, 1)]
+    run_case(wl, rows=rows)
+
+
+def test_single_loop_model():
+    wl = Workload("r1", 79, 1, 1, 2, 2, 96, 8, 4, [70, 129], 0.88, grid_rows(4, 1))
+    run_case(wl)
+
+
+def test_tagged_probe_exact_key_sets():
+    """Zero keys and tagged values: O is the mean plane index / position of
+    the attended keys, LSE = ln(#keys) (closed form, not the oracle)."""
+    R, D, L, W, d = 6, 4, 45, 9, 64
+    H = _h()
+    from self_speculative_verify_amd import RipeCache
+    for anchor in (0, 1):
+        cache = RipeCache(1, R, 1, 1, d, W, 1, L + D, D, anchor)
+        zero = np.zeros((1, 1, L, d), np.float32)
+
+        def tag(p, r):
+            v = np.zeros(d, np.float32)
+            v[0], v[1], v[2] = r, p, 1.0
+            return v
+        dv = np.stack([tag(p, R) for p in range(L)])[None, None]
+        wv = np.stack([np.stack([tag(p, r) for p in range(L - W, L)]) for r in range(1, R)])[None, :, None]
+        dev = lambda a: H.to_dev(f32_to_bf16(a).reshape(a.shape))
+        cache.append(0, [L], dev(zero), dev(dv), dev(np.zeros_like(wv)), dev(wv))
+        bv = np.stack([np.stack([tag(L + j, r) for j in range(D)]) for r in range(1, R + 1)])[None, :, None]
+        rows = grid_rows(D, R)
+        q = dev(np.random.default_rng(5).standard_normal((1, len(rows), 1, d)).astype(np.float32))
+        out, lse = cache.verify(0, rows, q, dev(np.zeros_like(bv)), dev(bv), D)
+        out, lse = out.cpu().double().numpy(), lse.cpu().double().numpy()
+        for k, (i, r) in enumerate(rows):
+            t = L + i
+            n = t + 1
+            beta = t - W if anchor == 0 else L - W
+            n_deep = min(max(beta, 0), L) if r < R else L
+            assert abs(lse[0, k, 0] - math.log(n)) < 1e-5
+            assert abs(out[0, k, 0, 0] - (R * n_deep + r * (n - n_deep)) / n) < 1e-5, (i, r)
+            assert abs(out[0, k, 0, 1] - t / 2) < 1e-4, (i, r)
+            assert abs(out[0, k, 0, 2] - 1.0) < 1e-6
+
+
+def test_block_independence_on_gpu():
+    """Query anchor with W >= D - 1: one D-row call equals two calls with the
+    first part of the block appended in between."""
+    H = _h()
+    wl = Workload("bi", 80, 1, 4, 4, 2, 64, 5, 6, [300, 41], 0.88, grid_rows(6, 4))
+    cache = H.make_cache(wl)
+    H.load_prefix(cache, wl)
+    q, bk, bv = H.verify_inputs(wl, 0)
+    full_o, full_l = cache.verify(0, wl.rows, q, bk, bv, 6)
+    k = 3
+    first = [(i, r) for (i, r) in wl.rows if i < k]
+    idx1 = [wl.rows.index(x) for x in first]
+    o1, l1 = cache.verify(0, first, q[:, idx1].contiguous(), bk, bv, 6)
+    R = wl.n_loops
+    cache.append(0, [k, k], bk[:, R - 1, :, :k], bv[:, R - 1, :, :k], bk[:, :R - 1, :, :k],
+                 bv[:, :R - 1, :, :k])
+    second = [(i - k, r) for (i, r) in wl.rows if i >= k]
+    idx2 = [wl.rows.index((i + k, r)) for (i, r) in second]
+    bk2 = torch.zeros_like(bk)
+    bv2 = torch.zeros_like(bv)
+    bk2[:, :, :, :6 - k] = bk[:, :, :, k:6]
+    bv2[:, :, :, :6 - k] = bv[:, :, :, k:6]
+    o2, l2 = cache.verify(0, second, q[:, idx2].contiguous(), bk2, bv2, 6 - k)
+    torch.cuda.synchronize()
+    so = torch.zeros_like(full_o)
+    sl = torch.zeros_like(full_l)
+    so[:, idx1], sl[:, idx1] = o1, l1
+    so[:, idx2], sl[:, idx2] = o2, l2
+    assert float((so - full_o).abs().max()) < 1e-5
+    assert float((sl - full_l).abs().max()) < 1e-5
