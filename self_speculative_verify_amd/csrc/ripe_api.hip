@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -71,6 +72,65 @@ bool view_ok(const ripe_kv_view& v) {
     for (int64_t x : s)
         if (x < 0 || x % 8) return false;
     return true;
+}
+
+// How one launch covers a call.  Row-heads (query row x query head of a KV
+// group) of a KV head: with 64 or more the "rows" kernel gives each wave 16*rt
+// of them and a workgroup 64*rt; with fewer the "keys" kernel gives a whole
+// workgroup 16*rt and splits the key tiles between its waves.  Committed
+// positions split into nc chunks of cl positions (a multiple of 32) when the
+// row blocks alone give too few workgroups for 256 compute units and the
+// chunks stay long enough that their partial states cost little next to the
+// keys they read.
+struct Plan {
+    bool rows_kernel;
+    int rt, nrb, nc, n_groups, M;
+    int64_t cl;
+    size_t ws_bytes;
+};
+
+int env_int(const char* name, int fallback) {
+    const char* e = std::getenv(name);
+    const int v = e ? std::atoi(e) : 0;
+    return v > 0 ? v : fallback;
+}
+
+Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here) {
+    // tuning and test overrides: workgroup target, row tiles, kernel (1 keys, 2 rows)
+    const int target = env_int("RIPE_ITEMS_TARGET", 512);
+    const int force_rt = env_int("RIPE_ROW_TILES", 0);
+    const int force_kernel = env_int("RIPE_KERNEL", 0);
+    const int force_min_chunk = env_int("RIPE_MIN_CHUNK", 0);
+    Plan p;
+    p.M = rows_here * (g.Hq / g.Hkv);
+    p.rows_kernel = force_kernel ? force_kernel == 2 : p.M >= 64;
+    const int64_t heads = (int64_t)g.B * g.Hkv;
+    int rows_per_item;
+    if (p.rows_kernel) {
+        p.rt = ripe::rows_max_row_tiles(g.d);
+        if (p.rt > 1 && heads * ((p.M + 64 * p.rt - 1) / (64 * p.rt)) < 256) p.rt = 1;
+        rows_per_item = 64;
+    } else {
+        p.rt = std::min(p.M <= 16 ? 1 : 2, ripe::keys_max_row_tiles(g.d));
+        rows_per_item = 16;
+    }
+    if (force_rt > 0) p.rt = std::min(force_rt, p.rows_kernel ? ripe::rows_max_row_tiles(g.d)
+                                                              : ripe::keys_max_row_tiles(g.d));
+    rows_per_item *= p.rt;
+    p.nrb = (p.M + rows_per_item - 1) / rows_per_item;
+    int64_t lmax = 0;
+    for (int b = 0; b < g.B; ++b) lmax = std::max<int64_t>(lmax, lens[b]);
+    const int64_t base = heads * p.nrb;
+    int64_t nc = 1;
+    if (base < target) {
+        const int64_t min_chunk = force_min_chunk ? force_min_chunk : std::max<int64_t>(256, 8 * rows_per_item);
+        nc = std::max<int64_t>(1, std::min<int64_t>((target + base - 1) / base, lmax / min_chunk));
+    }
+    p.cl = std::max<int64_t>(32, up((lmax + nc - 1) / nc, 32));
+    p.nc = (int)std::max<int64_t>(1, (lmax + p.cl - 1) / p.cl);
+    p.n_groups = (int)(heads * p.nc);
+    p.ws_bytes = p.nc > 1 ? (size_t)heads * p.nc * p.M * (g.d + 2) * sizeof(float) : 0;
+    return p;
 }
 
 ripe::View as_view(const ripe_kv_view& v) {
@@ -202,8 +262,15 @@ ripe_status ripe_append(ripe_cache* cache, int32_t layer, const int32_t* h_n_new
 }
 
 size_t ripe_workspace_bytes(const ripe_cache* cache, int32_t n_rows) {
-    if (!live(cache) || n_rows < 0) return 0;
-    return 0;
+    if (!live(cache) || n_rows <= 0) return 0;
+    const Geometry& g = cache->g;
+    const int32_t* lens = cache->lens.data();
+    size_t ws = 0;
+    for (int layer = 0; layer < g.n_layers; ++layer) {   // any layer may be verified
+        const int rows_here = std::min(ripe::kMaxRowsPerLaunch, (int)n_rows);
+        ws = std::max(ws, make_plan(g, lens + (size_t)layer * g.B, rows_here).ws_bytes);
+    }
+    return ws;
 }
 
 ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
@@ -252,10 +319,16 @@ ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
     a.R = g.R; a.d = g.d; a.n_blk = n_blk; a.anchor = g.anchor;
     a.W = g.W; a.CP = g.CP; a.WR = g.WR; a.WP = g.WP; a.NR = g.NR;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
+    const int32_t* lens = cache->lens.data() + (size_t)layer * g.B;
     for (int k0 = 0; k0 < n_rows; k0 += ripe::kMaxRowsPerLaunch) {
         a.rows_here = std::min(ripe::kMaxRowsPerLaunch, n_rows - k0);
         for (int k = 0; k < a.rows_here; ++k) a.rows[k] = rows[k0 + k];
-        if (ripe::launch_verify_valu(a, stream) != hipSuccess) return RIPE_EDEVICE;
+        const Plan p = make_plan(g, lens, a.rows_here);
+        a.M = p.M; a.nrb = p.nrb; a.nc = p.nc; a.cl = p.cl; a.n_groups = p.n_groups;
+        const hipError_t e = p.rows_kernel ? ripe::launch_verify_rows(a, p.rt, stream)
+                                           : ripe::launch_verify_keys(a, p.rt, stream);
+        if (e != hipSuccess) return RIPE_EDEVICE;
+        if (p.nc > 1 && ripe::launch_combine(a, stream) != hipSuccess) return RIPE_EDEVICE;
     }
     return RIPE_OK;
 }

@@ -81,11 +81,25 @@ struct VerifyArgs {
     int64_t W, CP, WR, WP, NR;
     float scale_log2;        // log2(e) / sqrt(d)
     int32_t rows_here;       // rows in this launch
+    // matrix-core plan: row-heads of one KV head split into blocks of 16*RT,
+    // committed positions split into nc chunks of cl (a multiple of 32)
+    int32_t M;               // row-heads per KV head in this launch (rows_here * group)
+    int32_t nrb;             // row blocks per KV head
+    int32_t nc;              // chunks of the longest sequence
+    int64_t cl;              // positions per chunk
+    int32_t n_groups;        // B * Hkv * nc
     // rows of this launch sorted by (loop, block offset):
     // bits 0..7 block offset, 8..15 loop, 16..31 row index in the call
     uint32_t rows[kMaxRowsPerLaunch];
 };
 
 hipError_t launch_verify_valu(const VerifyArgs& a, hipStream_t s);
+// matrix-core kernels: "keys" (waves split the key tiles of 16*rt row-heads)
+// and "rows" (each wave owns 16*rt row-heads; the workgroup 64*rt)
+int keys_max_row_tiles(int d);
+int rows_max_row_tiles(int d);
+hipError_t launch_verify_keys(const VerifyArgs& a, int rt, hipStream_t s);
+hipError_t launch_verify_rows(const VerifyArgs& a, int rt, hipStream_t s);
+hipError_t launch_combine(const VerifyArgs& a, hipStream_t s);
 
 }  // namespace ripe

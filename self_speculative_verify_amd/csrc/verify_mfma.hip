@@ -1,0 +1,985 @@
+// Matrix-core verification attention (gfx950, v_mfma_f32_16x16x32_bf16).
+//
+// The D x R verification grid puts D*R*(Hq/Hkv) query rows on every key tile
+// of the shared deepest-plane tail (page "Prefix Keys and Values Matter
+// Late", abstract: RIPE keeps loop R of every position, and verification runs
+// the block at every loop), so Q.K^T and P.V over the tail are dense
+// contractions and run on the matrix cores.
+//
+// A row-head is one (query row, query head of the KV group).  A work item is
+// (sequence b, KV head g, block of row-heads, chunk of committed positions);
+// its keys come in 32-row tiles of three kinds:
+//   deep tiles  - loop R, positions < e_row of each row-head (every chunk);
+//   ring tiles  - the window at loop r < R, one plane per loop present
+//                 (last chunk only);
+//   block tiles - the draft block at each loop present (last chunk only).
+// For one key tile and 16 row-heads a wave computes S^T = K.Q^T (lane =
+// row-head, registers = keys), masks, updates the online softmax in the log2
+// domain and accumulates O^T += V^T.P^T, with P split into two bf16 terms
+// (hi + lo) so the value weights keep ~16 significant bits.  K and V operands
+// are 16-byte pieces of the storage tiles, which hold keys as 32x32 blocks and
+// values transposed, in exactly the operand order of the instruction.
+//
+// Two kernels share that tile step:
+//   k_verify_rows - many row-heads per KV head (the D x R grid).  Each wave
+//                   owns 16*RTW row-heads; the deep tiles are staged once per
+//                   workgroup through a 4-stage LDS pipeline fed by direct
+//                   global->LDS loads and read by all four waves; ring and
+//                   block tiles, which only the waves holding that loop need,
+//                   are loaded by those waves alone.
+//   k_verify_keys - few row-heads (a wave, or a small grid).  The four waves
+//                   hold the same row-heads, split the key tiles between them
+//                   and merge their softmax states through LDS.
+// A single-chunk item writes O and LSE; otherwise each chunk writes its
+// partial state (m, l, O) and k_combine merges them.
+#include "ripe_internal.h"
+
+namespace ripe {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ inline f32x4 mfma(const uint4& a, const uint4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two floats -> two bf16 (round to nearest even) in one dword, lo first
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2_t));
+}
+
+// key offset (0..31) inside a tile of the e-th score register of a lane in
+// lane group q: registers 0..3 are keys 4q..4q+3, registers 4..7 keys 16+4q..
+__device__ inline int key_of(int e, int q) { return 16 * (e >> 2) + 4 * q + (e & 3); }
+
+template <int D>
+struct Frags {
+    uint4 k[D / 32][2];   // A operand of S^T: 16 keys x 32 dims, two key halves
+    uint4 v[D / 16];      // A operand of O^T: 16 value dims x 32 keys
+};
+
+// per-lane state of one 16-row-head tile
+template <int D>
+struct RowTile {
+    uint4 q[D / 32];      // B operand of S^T: row-head n, dims 32c + 8q..+8
+    float m, l;           // running max of the raw scores and partial sum of p
+    f32x4 o[D / 16];      // O^T: dims 16dt + 4q..+4 of row-head n
+    int ri;               // bits 0..7 block offset, 8..15 loop, bit 16 valid
+    int e;                // loop-R positions of this row-head end here (e_row)
+};
+#define RI_OK(x) (((x) >> 16) & 1)
+#define RI_R(x) (((x) >> 8) & 255)
+#define RI_I(x) ((x) & 255)
+
+// operand pieces of one tile: K at K + c*1024 + key*32 + 8q, V at V + e*32 + 8q
+template <int D>
+__device__ inline void load_frags(const uint16_t* K, const uint16_t* V, Frags<D>& f, int n, int q) {
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+            f.k[c][hf] = *reinterpret_cast<const uint4*>(K + c * 1024 + (16 * hf + n) * 32 + 8 * q);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        f.v[dt] = *reinterpret_cast<const uint4*>(V + (dt * 16 + n) * 32 + 8 * q);
+}
+
+// The same operand pieces from a tile pair staged in LDS by load_stage: piece
+// i of D/8 (K pieces, then V pieces) is a 1 KB block in which lane l's 16
+// bytes sit at l*16, so each ds_read_b128 is one conflict-free contiguous
+// read.  One asm block issues all reads and waits for them, so no output
+// register is live while its load is in flight; the compiler sees no LDS read
+// it could order against the in-flight global->LDS loads of other stages.  The
+// outputs are early-clobber: later reads of the block still use the address.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+#define RD(i) "ds_read_b128 %" #i ", %[a] offset:" #i "*1024\n"
+template <int D>
+__device__ inline void lds_frags(const uint16_t* stage, Frags<D>& f, int n, int q);
+template <>
+__device__ inline void lds_frags<64>(const uint16_t* stage, Frags<64>& f, int n, int q) {
+    const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)stage + (q * 16 + n) * 16;
+    u32x4 r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(RD(0) RD(1) RD(2) RD(3) RD(4) RD(5) RD(6) RD(7) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+                 : [a] "v"(addr) : "memory");
+    f.k[0][0] = __builtin_bit_cast(uint4, r0); f.k[0][1] = __builtin_bit_cast(uint4, r1);
+    f.k[1][0] = __builtin_bit_cast(uint4, r2); f.k[1][1] = __builtin_bit_cast(uint4, r3);
+    f.v[0] = __builtin_bit_cast(uint4, r4); f.v[1] = __builtin_bit_cast(uint4, r5);
+    f.v[2] = __builtin_bit_cast(uint4, r6); f.v[3] = __builtin_bit_cast(uint4, r7);
+}
+template <>
+__device__ inline void lds_frags<96>(const uint16_t* stage, Frags<96>& f, int n, int q) {
+    const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)stage + (q * 16 + n) * 16;
+    u32x4 r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11;
+    asm volatile(RD(0) RD(1) RD(2) RD(3) RD(4) RD(5) RD(6) RD(7) RD(8) RD(9) RD(10) RD(11)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7),
+                   "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11)
+                 : [a] "v"(addr) : "memory");
+    f.k[0][0] = __builtin_bit_cast(uint4, r0); f.k[0][1] = __builtin_bit_cast(uint4, r1);
+    f.k[1][0] = __builtin_bit_cast(uint4, r2); f.k[1][1] = __builtin_bit_cast(uint4, r3);
+    f.k[2][0] = __builtin_bit_cast(uint4, r4); f.k[2][1] = __builtin_bit_cast(uint4, r5);
+    f.v[0] = __builtin_bit_cast(uint4, r6); f.v[1] = __builtin_bit_cast(uint4, r7);
+    f.v[2] = __builtin_bit_cast(uint4, r8); f.v[3] = __builtin_bit_cast(uint4, r9);
+    f.v[4] = __builtin_bit_cast(uint4, r10); f.v[5] = __builtin_bit_cast(uint4, r11);
+}
+template <>
+__device__ inline void lds_frags<128>(const uint16_t* stage, Frags<128>& f, int n, int q) {
+    const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)stage + (q * 16 + n) * 16;
+    u32x4 r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11, r12, r13, r14, r15;
+    asm volatile(RD(0) RD(1) RD(2) RD(3) RD(4) RD(5) RD(6) RD(7) RD(8) RD(9) RD(10) RD(11)
+                 RD(12) RD(13) RD(14) RD(15) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7),
+                   "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13), "=&v"(r14), "=&v"(r15)
+                 : [a] "v"(addr) : "memory");
+    f.k[0][0] = __builtin_bit_cast(uint4, r0); f.k[0][1] = __builtin_bit_cast(uint4, r1);
+    f.k[1][0] = __builtin_bit_cast(uint4, r2); f.k[1][1] = __builtin_bit_cast(uint4, r3);
+    f.k[2][0] = __builtin_bit_cast(uint4, r4); f.k[2][1] = __builtin_bit_cast(uint4, r5);
+    f.k[3][0] = __builtin_bit_cast(uint4, r6); f.k[3][1] = __builtin_bit_cast(uint4, r7);
+    f.v[0] = __builtin_bit_cast(uint4, r8); f.v[1] = __builtin_bit_cast(uint4, r9);
+    f.v[2] = __builtin_bit_cast(uint4, r10); f.v[3] = __builtin_bit_cast(uint4, r11);
+    f.v[4] = __builtin_bit_cast(uint4, r12); f.v[5] = __builtin_bit_cast(uint4, r13);
+    f.v[6] = __builtin_bit_cast(uint4, r14); f.v[7] = __builtin_bit_cast(uint4, r15);
+}
+#undef RD
+
+// max over lanes l, l^16, l^32, l^48 (the four copies of a row-head)
+__device__ inline float max_lane_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// One key tile against one row tile.  Scores stay in raw units; c = log2(e)/sqrt(d)
+// is folded into the exponent, p = 2^(s*c - m*c).  `full`: every key of the
+// tile is valid for every row-head of the tile (no masking needed).
+template <int D>
+__device__ inline void tile_update(RowTile<D>& rt, const Frags<D>& f, bool full,
+                                   const bool (&valid)[8], float c) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+        s0 = mfma(f.k[k][0], rt.q[k], s0);
+        s1 = mfma(f.k[k][1], rt.q[k], s1);
+    }
+    float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    if (!full) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = valid[e] ? x[e] : -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    bm = max_lane_groups(bm);
+    const float mo = rt.m;
+    const float mn = fmaxf(mo, bm);
+    const float ms = mn == -INFINITY ? 0.f : mn;     // finite reference for the exponents
+    const float nmc = -ms * c;
+    // exactly 1 when the max did not move (mo - ms == 0), so l and O stay in step
+    const float alpha = __builtin_amdgcn_exp2f((mo - ms) * c);
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c, nmc));
+        ps += p[e];
+    }
+    rt.m = mn;
+    rt.l = fmaf(rt.l, alpha, ps);
+    // P = hi + lo, both bf16: hi = round(p), lo = round(p - hi)
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+        hi[e2] = pack_bf16(p[2 * e2], p[2 * e2 + 1]);
+        const float h0 = __uint_as_float(hi[e2] << 16), h1 = __uint_as_float(hi[e2] & 0xffff0000u);
+        lo[e2] = pack_bf16(p[2 * e2] - h0, p[2 * e2 + 1] - h1);
+    }
+    const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    if (__any(mo != mn)) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            rt.o[dt][0] *= alpha; rt.o[dt][1] *= alpha;
+            rt.o[dt][2] *= alpha; rt.o[dt][3] *= alpha;
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        rt.o[dt] = mfma(f.v[dt], phi, rt.o[dt]);
+        rt.o[dt] = mfma(f.v[dt], plo, rt.o[dt]);
+    }
+}
+
+// ---------------------------------------------------------------- item
+
+struct Item {
+    int b, g, c, rb, nc_b;
+    bool last;
+    int L;
+    int nsl, ring_top, ring_base;   // ring slot sl < nsl holds ring_base + sl (- WR past ring_top)
+};
+
+// XCD-aware decode: the row blocks of one (b, g, chunk) share blockIdx % 8,
+// so they run on one XCD and share its L2.
+__device__ inline bool decode_item(const VerifyArgs& a, Item& it) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int grp = (slot / a.nrb) * 8 + xcd;
+    it.rb = slot % a.nrb;
+    if (grp >= a.n_groups) return false;
+    it.c = grp % a.nc;
+    const int bg = grp / a.nc;
+    it.g = bg % a.Hkv;
+    it.b = bg / a.Hkv;
+    it.L = a.lens[it.b];
+    it.nc_b = it.L > 0 ? (int)((it.L + a.cl - 1) / a.cl) : 1;
+    if (it.c >= it.nc_b) return false;
+    it.last = it.c == it.nc_b - 1;
+    it.nsl = (int)min(a.WR, (int64_t)it.L);
+    it.ring_top = it.nsl > 0 ? (int)((it.L - 1) % a.WR) : 0;
+    it.ring_base = it.L - 1 - it.ring_top;
+    return true;
+}
+
+// e_row: committed positions [0, e_row) are read at loop R
+__device__ inline int e_row(const VerifyArgs& a, int L, int i, int r) {
+    if (r == a.R) return L;
+    const int64_t beta = a.anchor == 0 ? (int64_t)L + i - a.W : (int64_t)L - a.W;
+    return (int)(beta < 0 ? 0 : (beta > L ? L : beta));
+}
+
+// the launch's row table, copied from the kernel arguments into LDS once
+__device__ inline void stage_rows(const VerifyArgs& a, uint32_t* s_rows) {
+    for (int k = threadIdx.x; k < a.rows_here; k += blockDim.x) s_rows[k] = a.rows[k];
+}
+
+template <int D>
+__device__ inline void init_row(const VerifyArgs& a, const uint32_t* s_rows, const Item& it, int u,
+                                int q, RowTile<D>& rt) {
+    const bool ok = u < a.M;
+    const uint32_t rw = s_rows[ok ? u / a.group : 0];
+    const int ii = rw & 255, rr = (rw >> 8) & 255;
+    rt.ri = ii | (rr << 8) | (ok ? 1 << 16 : 0);
+    rt.e = e_row(a, it.L, ii, rr);
+    rt.m = -INFINITY;
+    rt.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) rt.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int orig = (int)(rw >> 16), h = it.g * a.group + (ok ? u % a.group : 0);
+    const uint16_t* qp = a.q + (((int64_t)it.b * a.n_rows + orig) * a.Hq + h) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+        rt.q[c] = ok ? *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * q) : make_uint4(0, 0, 0, 0);
+}
+
+// masks of one row tile against a deep / ring / block tile; false = the tile
+// holds no key of any row-head of this row tile
+template <int D>
+__device__ inline int mask_deep(const RowTile<D>& rt, int base, int d1, int q, bool (&v)[8]) {
+    const int lim = min(rt.e, d1);
+    const bool mine = RI_OK(rt.ri) && base < lim;
+    if (!__any(mine)) return 0;
+    if (__all(!RI_OK(rt.ri) || base + 32 <= lim)) return 2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = mine && base + key_of(e, q) < lim;
+    return 1;
+}
+template <int D>
+__device__ inline int mask_ring(const RowTile<D>& rt, const Item& it, int WR, int r, int base,
+                                int q, bool (&v)[8]) {
+    const bool mine = RI_OK(rt.ri) && RI_R(rt.ri) == r && rt.e < it.L;
+    if (!__any(mine)) return 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int sl = base + key_of(e, q);
+        const int pos = it.ring_base + sl - (sl > it.ring_top ? WR : 0);
+        v[e] = mine && sl < it.nsl && pos >= rt.e;
+    }
+    return 1;
+}
+template <int D>
+__device__ inline int mask_block(const RowTile<D>& rt, int r, int base, int q, bool (&v)[8]) {
+    const bool mine = RI_OK(rt.ri) && RI_R(rt.ri) == r;
+    if (!__any(mine)) return 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = mine && base + key_of(e, q) <= RI_I(rt.ri);
+    return 1;
+}
+
+// stage 32 draft-block keys/values (caller's [token][dim] layout) into a
+// wave-private LDS tile pair in the storage's operand order
+template <int D>
+__device__ inline void stage_block(const VerifyArgs& a, const uint16_t* K, const uint16_t* V,
+                                   int base, uint16_t* sk, uint16_t* sv, int lane) {
+    for (int it = lane; it < 32 * (D / 8); it += 64) {
+        const int key = it / (D / 8), e0 = (it % (D / 8)) * 8;
+        const int jj = base + key;
+        uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+        if (jj < a.n_blk) {
+            kx = *reinterpret_cast<const uint4*>(K + jj * a.bk.st + e0);
+            vx = *reinterpret_cast<const uint4*>(V + jj * a.bv.st + e0);
+        }
+        *reinterpret_cast<uint4*>(sk + key_off(key, e0, D)) = kx;
+        const uint32_t w[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc)
+            sv[val_off(key, e0 + cc, D)] = (uint16_t)(w[cc >> 1] >> (16 * (cc & 1)));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// final (single chunk) or partial (multi-chunk) result of one row tile whose
+// l is already summed over the lane groups
+template <int D>
+__device__ inline void write_result(const VerifyArgs& a, const uint32_t* s_rows, const Item& it,
+                                    const RowTile<D>& rt, int u, int q) {
+    if (!RI_OK(rt.ri)) return;
+    const uint32_t rw = s_rows[u / a.group];
+    const int orig = (int)(rw >> 16), h = it.g * a.group + u % a.group;
+    if (it.nc_b == 1) {
+        const float inv = 1.f / rt.l;
+        float* op = a.out + (((int64_t)it.b * a.n_rows + orig) * a.Hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+            *reinterpret_cast<float4*>(op + dt * 16 + 4 * q) =
+                make_float4(rt.o[dt][0] * inv, rt.o[dt][1] * inv, rt.o[dt][2] * inv, rt.o[dt][3] * inv);
+        if (q == 0)
+            a.lse[((int64_t)it.b * a.n_rows + orig) * a.Hq + h] = (rt.m * a.scale_log2 + log2f(rt.l)) * kLn2;
+    } else {
+        const int64_t pidx = (((int64_t)it.b * a.Hkv + it.g) * a.nc + it.c) * a.M + u;
+        float* po = a.part + pidx * (D + 2);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            *reinterpret_cast<float2*>(po + dt * 16 + 4 * q) = make_float2(rt.o[dt][0], rt.o[dt][1]);
+            *reinterpret_cast<float2*>(po + dt * 16 + 4 * q + 2) = make_float2(rt.o[dt][2], rt.o[dt][3]);
+        }
+        // partial max in the log2 domain (-inf stays -inf)
+        if (q == 0) *reinterpret_cast<float2*>(po + D) = make_float2(rt.m * a.scale_log2, rt.l);
+    }
+}
+
+template <int D>
+__device__ inline void sum_lane_groups(RowTile<D>& rt) {
+    rt.l += __shfl_xor(rt.l, 16);
+    rt.l += __shfl_xor(rt.l, 32);
+}
+
+// ---------------------------------------------------------------- many rows
+
+// Issue the global->LDS loads of one K+V tile pair into an LDS stage.  The
+// pair is D/8 blocks of 1 KB (D/16 of K, then D/16 of V); this thread's wave
+// loads blocks j*4 + wave (j < D/32).  Within a block, lane l loads the 16 bytes the
+// matrix operand wants in lane l (key or value row l%16, columns 8*(l/16)..),
+// which the LDS write puts at l*16.
+template <int D>
+__device__ inline void load_stage(const uint16_t* Kt, const uint16_t* Vt, uint16_t* stage, int wave,
+                                  int lane) {
+    constexpr int BLOCKS = D / 8;                     // 1 KB blocks in a K+V pair
+    static_assert(BLOCKS % 4 == 0, "four waves share the blocks");
+    const int src_off = (lane & 15) * 32 + (lane >> 4) * 8;
+#pragma unroll
+    for (int j = 0; j < BLOCKS / 4; ++j) {
+        const int blk = j * 4 + wave;
+        const uint16_t* src = (blk < BLOCKS / 2 ? Kt + blk * 512 : Vt + (blk - BLOCKS / 2) * 512) + src_off;
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                         (void __attribute__((address_space(3)))*)(stage + blk * 512),
+                                         16, 0, 0);
+    }
+}
+
+// Eight waves: waves w and w+4 own the same 16*RTW row-heads and take the
+// even and odd tiles of the stream (key halves kh = 0, 1), so every SIMD runs
+// two independent tile steps; their softmax states merge through LDS at the end.
+template <int D, int RTW>
+__global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
+    constexpr int TILE = 32 * D;                 // elements of one K or V tile
+    // LDS pipeline stages (one tile per half each); the workgroup's LDS stays
+    // below 128 KB
+    constexpr int S = D == 128 ? 3 : 4;
+    constexpr int PER_THREAD = D / 32;           // global->LDS loads per thread per tile
+    constexpr int PF = D / 16;                   // prefetched draft-block pieces per lane
+    constexpr int MS = D / 4 + 2;                // floats of one lane's state in the merge
+    __shared__ __attribute__((aligned(16))) uint16_t s_tile[S][2][2 * TILE];
+    __shared__ uint32_t s_rows[kMaxRowsPerLaunch];
+    __shared__ int s_E, s_nl, s_loops[kMaxRowsPerLaunch];
+    static_assert(4 * RTW * 64 * MS * 4 <= (int)sizeof(s_tile), "merge buffer");
+    static_assert(4 * 2 * TILE * 2 <= (int)sizeof(s_tile), "per-wave block scratch");
+
+    Item it;
+    if (!decode_item(a, it)) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rw = wave & 3, kh = wave >> 2;     // row group, key half
+    const int n = lane & 15, q = lane >> 4;
+    const int G = a.group;
+    const int u_blk = it.rb * 64 * RTW;          // first row-head of the workgroup
+    const int u_w = u_blk + rw * 16 * RTW;       // first row-head of this wave
+    stage_rows(a, s_rows);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        // loops r < R present in the workgroup (rows are sorted by loop): ring planes
+        const int k_lo = u_blk / G;
+        const int k_hi = min(a.rows_here, (min(a.M, u_blk + 64 * RTW) + G - 1) / G);
+        int nl = 0, prev = -1;
+        for (int k = k_lo; k < k_hi; ++k) {
+            const int r = (s_rows[k] >> 8) & 255;
+            if (r != prev && r < a.R) s_loops[nl++] = r;
+            prev = r;
+        }
+        s_nl = nl;
+        s_E = 0;
+    }
+
+    RowTile<D> rt[RTW];
+    int e_max = 0;
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+        init_row<D>(a, s_rows, it, u_w + 16 * t + n, q, rt[t]);
+        if (RI_OK(rt[t].ri)) e_max = max(e_max, rt[t].e);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) e_max = max(e_max, __shfl_xor(e_max, o));
+    __syncthreads();
+    if (lane == 0) atomicMax(&s_E, e_max);
+
+    // this wave's loops (ascending) with their largest block offsets
+    int wl[2] = {-1, -1}, wimax[2] = {0, 0}, n_wl = 0;
+    bool wl_more = false;                         // more than two loops: slow path
+    {
+        int done = 0;
+        for (int round = 0; round < 3; ++round) {
+            int r = 1 << 30;
+#pragma unroll
+            for (int t = 0; t < RTW; ++t)
+                if (RI_OK(rt[t].ri) && !((done >> t) & 1)) r = min(r, (int)RI_R(rt[t].ri));
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) r = min(r, __shfl_xor(r, o));
+            r = __builtin_amdgcn_readfirstlane(r);
+            if (r == 1 << 30) break;
+            if (round == 2) { wl_more = true; break; }
+            int im = 0;
+#pragma unroll
+            for (int t = 0; t < RTW; ++t)
+                if (RI_OK(rt[t].ri) && RI_R(rt[t].ri) == r) {
+                    im = max(im, (int)RI_I(rt[t].ri));
+                    done |= 1 << t;
+                }
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) im = max(im, __shfl_xor(im, o));
+            wl[round] = r;
+            wimax[round] = __builtin_amdgcn_readfirstlane(im);
+            n_wl = round + 1;
+        }
+    }
+    // prefetch the draft-block rows of up to two loops (keys < 8) into registers;
+    // piece pc = ((slot*2 + kv)*8 + key)*(D/8) + chunk, lane holds pc = lane + 64k
+    const bool pf_ok = kh == 0 && it.last && !wl_more && (n_wl < 1 || wimax[0] < 8) &&
+                       (n_wl < 2 || wimax[1] < 8);
+    uint4 pf[PF];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+        const int pc = lane + 64 * k;
+        const int c8 = pc % (D / 8), rest = pc / (D / 8);
+        const int key = rest % 8, kv = (rest / 8) % 2, sl = rest / 16;
+        pf[k] = make_uint4(0, 0, 0, 0);
+        if (pf_ok && sl < n_wl && key < a.n_blk && key <= wimax[sl]) {
+            const View& vw = kv ? a.bv : a.bk;
+            const uint16_t* src = vw.p + it.b * vw.sb + (int64_t)(wl[sl] - 1) * vw.sp +
+                                  it.g * vw.sh + key * vw.st + c8 * 8;
+            pf[k] = *reinterpret_cast<const uint4*>(src);
+        }
+    }
+    __syncthreads();
+    const int E = s_E;
+    const int nl = s_nl;
+
+    const int d0 = (int)((int64_t)it.c * a.cl);
+    const int d1 = (int)min((int64_t)d0 + a.cl, (int64_t)E);
+    const int n_deep = d1 > d0 ? (d1 - d0 + 31) / 32 : 0;
+    const int ring_tiles = (it.last && a.R > 1 && it.nsl > 0) ? (it.nsl + 31) / 32 : 0;
+    const int n_tiles = n_deep + nl * ring_tiles;
+    const float sl2 = a.scale_log2;
+
+    const int64_t dreg = ((int64_t)it.b * a.Hkv + it.g) * a.CP * D;
+    const int64_t rreg0 = ((int64_t)it.b * a.Hkv + it.g) * a.NR * a.WP * D;
+    // tile t of the stream: deep tiles of the chunk, then the ring tiles of each
+    // loop; iteration i holds tiles 2i (half 0) and 2i+1 (half 1)
+    const int n_iter = (n_tiles + 1) / 2;
+    const int n_mine = kh == 0 ? n_iter : n_tiles / 2;   // iterations with a tile for this half
+    auto issue = [&](int i) {
+        const int t = 2 * i + kh;
+        if (t >= n_tiles) return;
+        const uint16_t *Kt, *Vt;
+        if (t < n_deep) {
+            const int64_t off = dreg + (int64_t)(d0 + 32 * t) * D;
+            Kt = a.deep_k + off;
+            Vt = a.deep_v + off;
+        } else {
+            const int p = (t - n_deep) / ring_tiles, st = (t - n_deep) % ring_tiles;
+            const int64_t off = rreg0 + (int64_t)(s_loops[p] - 1) * a.WP * D + (int64_t)st * TILE;
+            Kt = a.ring_k + off;
+            Vt = a.ring_v + off;
+        }
+        load_stage<D>(Kt, Vt, s_tile[i % S][kh], rw, lane);
+    };
+    for (int i = 0; i < S - 1 && i < n_iter; ++i) issue(i);
+    for (int i = 0; i < n_iter; ++i) {
+        // this thread's loads of iteration i are done when at most its loads of
+        // the later issued iterations are outstanding (s_waitcnt vmcnt(N); 0xF70
+        // leaves expcnt and lgkmcnt unconstrained)
+        const int later = max(0, min(i + S - 2, n_mine - 1) - i);
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * PER_THREAD));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(0xF70 | PER_THREAD);
+        else __builtin_amdgcn_s_waitcnt(0xF70);
+        // every wave's part of iteration i is in LDS, and every wave finished
+        // reading stage (i-1) % S (its reads complete inside lds_frags)
+        __builtin_amdgcn_s_barrier();
+        if (i + S - 1 < n_iter) issue(i + S - 1);
+        const int t = 2 * i + kh;
+        if (t >= n_tiles) continue;
+        const uint16_t* stage = s_tile[i % S][kh];
+        Frags<D> f;
+        bool have = false;
+        if (t < n_deep) {
+            const int base = d0 + 32 * t;
+#pragma unroll
+            for (int tr = 0; tr < RTW; ++tr) {
+                bool v[8];
+                const int mode = mask_deep<D>(rt[tr], base, d1, q, v);
+                if (mode) {
+                    if (!have) lds_frags<D>(stage, f, n, q);
+                    have = true;
+                    tile_update<D>(rt[tr], f, mode == 2, v, sl2);
+                }
+            }
+        } else {
+            const int p = (t - n_deep) / ring_tiles, base = ((t - n_deep) % ring_tiles) * 32;
+            const int r = s_loops[p];
+#pragma unroll
+            for (int tr = 0; tr < RTW; ++tr) {
+                bool v[8];
+                if (mask_ring<D>(rt[tr], it, (int)a.WR, r, base, q, v)) {
+                    if (!have) lds_frags<D>(stage, f, n, q);
+                    have = true;
+                    tile_update<D>(rt[tr], f, false, v, sl2);
+                }
+            }
+        }
+    }
+
+    // merge half 1 into half 0 (lane-wise: both hold the same row-heads)
+    __syncthreads();
+    float* s_m = reinterpret_cast<float*>(&s_tile[0][0][0]);
+    if (kh == 1) {
+#pragma unroll
+        for (int tr = 0; tr < RTW; ++tr) {
+            float* dst = s_m + ((rw * RTW + tr) * 64 + lane) * MS;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[dt * 4 + j] = rt[tr].o[dt][j];
+            dst[D / 4] = rt[tr].m;
+            dst[D / 4 + 1] = rt[tr].l;
+        }
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+        for (int tr = 0; tr < RTW; ++tr) {
+            const float* src = s_m + ((rw * RTW + tr) * 64 + lane) * MS;
+            const float m2 = src[D / 4], l2 = src[D / 4 + 1];
+            const float mn = fmaxf(rt[tr].m, m2);
+            const float w1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((rt[tr].m - mn) * sl2);
+            const float w2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * sl2);
+            rt[tr].m = mn;
+            rt[tr].l = rt[tr].l * w1 + l2 * w2;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) rt[tr].o[dt][j] = rt[tr].o[dt][j] * w1 + src[dt * 4 + j] * w2;
+        }
+    }
+    __syncthreads();                               // merge buffer free again
+    if (kh == 1) return;
+
+    if (it.last) {
+        uint16_t* sk = &s_tile[0][0][0] + rw * 2 * TILE;   // per-wave scratch in the stages
+        uint16_t* sv = sk + TILE;
+        // draft-block keys of the wave's loops: from the prefetched registers when
+        // they fit, else staged straight from the caller's buffer
+        for (int sl = 0; sl < n_wl; ++sl) {
+            const int r = wl[sl];
+            const uint16_t* bK = a.bk.p + it.b * a.bk.sb + (int64_t)(r - 1) * a.bk.sp + it.g * a.bk.sh;
+            const uint16_t* bV = a.bv.p + it.b * a.bv.sb + (int64_t)(r - 1) * a.bv.sp + it.g * a.bv.sh;
+            for (int base = 0; base <= wimax[sl]; base += 32) {
+                if (pf_ok) {
+                    for (int z = lane; z < 2 * TILE / 8; z += 64)
+                        *reinterpret_cast<uint4*>(sk + z * 8) = make_uint4(0, 0, 0, 0);
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                    for (int k = 0; k < PF; ++k) {
+                        const int pc = lane + 64 * k;
+                        const int c8 = pc % (D / 8), rest = pc / (D / 8);
+                        const int key = rest % 8, kv = (rest / 8) % 2, psl = rest / 16;
+                        if (psl != sl) continue;
+                        if (kv == 0) {
+                            *reinterpret_cast<uint4*>(sk + key_off(key, c8 * 8, D)) = pf[k];
+                        } else {
+                            const uint32_t w[4] = {pf[k].x, pf[k].y, pf[k].z, pf[k].w};
+#pragma unroll
+                            for (int cc = 0; cc < 8; ++cc)
+                                sv[val_off(key, c8 * 8 + cc, D)] = (uint16_t)(w[cc >> 1] >> (16 * (cc & 1)));
+                        }
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                } else {
+                    stage_block<D>(a, bK, bV, base, sk, sv, lane);
+                }
+                Frags<D> f;
+                load_frags<D>(sk, sv, f, n, q);
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int tr = 0; tr < RTW; ++tr) {
+                    bool v[8];
+                    if (mask_block<D>(rt[tr], r, base, q, v)) tile_update<D>(rt[tr], f, false, v, sl2);
+                }
+            }
+        }
+        if (wl_more) {
+            // loops beyond the first two (unusual row sets): smallest remaining first
+            int done = 0;
+#pragma unroll
+            for (int t = 0; t < RTW; ++t)
+                if (RI_OK(rt[t].ri) && (RI_R(rt[t].ri) == wl[0] || RI_R(rt[t].ri) == wl[1])) done |= 1 << t;
+            for (;;) {
+                int r = 1 << 30;
+#pragma unroll
+                for (int t = 0; t < RTW; ++t)
+                    if (RI_OK(rt[t].ri) && !((done >> t) & 1)) r = min(r, (int)RI_R(rt[t].ri));
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) r = min(r, __shfl_xor(r, o));
+                r = __builtin_amdgcn_readfirstlane(r);
+                if (r == 1 << 30) break;
+                int im = 0;
+#pragma unroll
+                for (int t = 0; t < RTW; ++t)
+                    if (RI_OK(rt[t].ri) && RI_R(rt[t].ri) == r) {
+                        im = max(im, (int)RI_I(rt[t].ri));
+                        done |= 1 << t;
+                    }
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) im = max(im, __shfl_xor(im, o));
+                im = __builtin_amdgcn_readfirstlane(im);
+                const uint16_t* bK = a.bk.p + it.b * a.bk.sb + (int64_t)(r - 1) * a.bk.sp + it.g * a.bk.sh;
+                const uint16_t* bV = a.bv.p + it.b * a.bv.sb + (int64_t)(r - 1) * a.bv.sp + it.g * a.bv.sh;
+                for (int base = 0; base <= im; base += 32) {
+                    stage_block<D>(a, bK, bV, base, sk, sv, lane);
+                    Frags<D> f;
+                    load_frags<D>(sk, sv, f, n, q);
+                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                    for (int tr = 0; tr < RTW; ++tr) {
+                        bool v[8];
+                        if (mask_block<D>(rt[tr], r, base, q, v)) tile_update<D>(rt[tr], f, false, v, sl2);
+                    }
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int tr = 0; tr < RTW; ++tr) {
+        sum_lane_groups<D>(rt[tr]);
+        write_result<D>(a, s_rows, it, rt[tr], u_w + 16 * tr + n, q);
+    }
+}
+
+// ---------------------------------------------------------------- few rows
+
+constexpr int kMaxLoopsWG = 64;
+
+struct Job {
+    int kind;              // 0 deep, 1 ring, 2 block
+    int r;
+    int base;              // first position (deep), slot (ring), block offset (block)
+    const uint16_t* K;
+    const uint16_t* V;
+};
+
+template <int D, int RT>
+__global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
+    constexpr int kStage = 4 * 2 * 32 * D;             // uint16: per-wave block tiles
+    constexpr int kMerge = 2 * RT * 16 * (D + 2);      // floats: merge buffers
+    constexpr int kLds = (kStage * 2 > kMerge * 4) ? kStage * 2 : kMerge * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char s_raw[kLds];
+    __shared__ int s_loop[kMaxLoopsWG], s_imax[kMaxLoopsWG], s_blkjob[kMaxLoopsWG + 1];
+    __shared__ int s_nloops;
+    __shared__ uint32_t s_rows[kMaxRowsPerLaunch];
+
+    Item it;
+    if (!decode_item(a, it)) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n = lane & 15, q = lane >> 4;
+    const int G = a.group;
+    const int u_base = it.rb * 16 * RT;
+    stage_rows(a, s_rows);
+    __syncthreads();
+    uint16_t* const sk = reinterpret_cast<uint16_t*>(s_raw) + wave * 2 * 32 * D;
+    uint16_t* const sv = sk + 32 * D;
+    float (*s_st)[RT][16][D + 2] = reinterpret_cast<float (*)[RT][16][D + 2]>(s_raw);
+
+    RowTile<D> rt[RT];
+    int E = 0;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        init_row<D>(a, s_rows, it, u_base + 16 * t + n, q, rt[t]);
+        if (RI_OK(rt[t].ri)) E = max(E, rt[t].e);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) E = max(E, __shfl_xor(E, o));
+    E = __builtin_amdgcn_readfirstlane(E);
+
+    const int k_lo = u_base / G;
+    const int k_hi = min(a.rows_here, (min(a.M, u_base + 16 * RT) + G - 1) / G);
+    if (threadIdx.x == 0) {
+        int nl = 0, prev = -1;
+        for (int k = k_lo; k < k_hi; ++k) {
+            const uint32_t rw = s_rows[k];
+            const int rr = (rw >> 8) & 255, ii = rw & 255;
+            if (rr != prev) {
+                s_loop[nl] = rr;
+                s_imax[nl] = ii;
+                ++nl;
+                prev = rr;
+            } else {
+                s_imax[nl - 1] = max(ii, s_imax[nl - 1]);
+            }
+        }
+        s_blkjob[0] = 0;
+        for (int p = 0; p < nl; ++p) s_blkjob[p + 1] = s_blkjob[p] + (s_imax[p] + 32) / 32;
+        s_nloops = nl;
+    }
+    __syncthreads();
+    const int nloops = s_nloops;
+    const int d0 = (int)((int64_t)it.c * a.cl);
+    const int d1 = (int)min((int64_t)d0 + a.cl, (int64_t)E);
+    const int n_deep = d1 > d0 ? (d1 - d0 + 31) / 32 : 0;
+    const int ring_tiles = (it.last && a.R > 1 && it.nsl > 0) ? (it.nsl + 31) / 32 : 0;
+    int n_ring_planes = 0;
+    if (ring_tiles > 0)
+        for (int p = 0; p < nloops; ++p) n_ring_planes += s_loop[p] < a.R;
+    const int n_ring = n_ring_planes * ring_tiles;
+    const int n_block = it.last ? s_blkjob[nloops] : 0;
+    const int n_jobs = n_deep + n_ring + n_block;
+    const int64_t dreg = ((int64_t)it.b * a.Hkv + it.g) * a.CP * D;
+    const int64_t rreg0 = ((int64_t)it.b * a.Hkv + it.g) * a.NR * a.WP * D;
+    const float sl2 = a.scale_log2;
+
+    auto job_of = [&](int j) -> Job {
+        Job jb;
+        if (j < n_deep) {
+            jb.kind = 0;
+            jb.r = a.R;
+            jb.base = d0 + j * 32;
+            jb.K = a.deep_k + dreg + (int64_t)jb.base * D;
+            jb.V = a.deep_v + dreg + (int64_t)jb.base * D;
+            return jb;
+        }
+        j -= n_deep;
+        if (j < n_ring) {
+            const int pl = j / ring_tiles, st = j % ring_tiles;
+            int p = 0, seen = -1;
+            for (; p < nloops; ++p) {
+                seen += s_loop[p] < a.R;
+                if (seen == pl) break;
+            }
+            jb.kind = 1;
+            jb.r = s_loop[p];
+            jb.base = st * 32;
+            const int64_t rreg = rreg0 + (int64_t)(jb.r - 1) * a.WP * D;
+            jb.K = a.ring_k + rreg + (int64_t)jb.base * D;
+            jb.V = a.ring_v + rreg + (int64_t)jb.base * D;
+            return jb;
+        }
+        j -= n_ring;
+        int p = 0;
+        while (s_blkjob[p + 1] <= j) ++p;
+        jb.kind = 2;
+        jb.r = s_loop[p];
+        jb.base = (j - s_blkjob[p]) * 32;
+        jb.K = a.bk.p + it.b * a.bk.sb + (int64_t)(jb.r - 1) * a.bk.sp + it.g * a.bk.sh;
+        jb.V = a.bv.p + it.b * a.bv.sb + (int64_t)(jb.r - 1) * a.bv.sp + it.g * a.bv.sh;
+        return jb;
+    };
+
+    for (int j = wave; j < n_jobs; j += 4) {
+        const Job jb = job_of(j);
+        const int kind = __builtin_amdgcn_readfirstlane(jb.kind);
+        const int jr = __builtin_amdgcn_readfirstlane(jb.r);
+        const int base = __builtin_amdgcn_readfirstlane(jb.base);
+        Frags<D> f;
+        if (kind == 2) {
+            stage_block<D>(a, jb.K, jb.V, base, sk, sv, lane);
+            load_frags<D>(sk, sv, f, n, q);
+            __builtin_amdgcn_wave_barrier();
+        } else {
+            load_frags<D>(jb.K, jb.V, f, n, q);
+        }
+#pragma unroll
+        for (int tr = 0; tr < RT; ++tr) {
+            bool v[8];
+            int mode;
+            if (kind == 0) mode = mask_deep<D>(rt[tr], base, d1, q, v);
+            else if (kind == 1) mode = mask_ring<D>(rt[tr], it, (int)a.WR, jr, base, q, v);
+            else mode = mask_block<D>(rt[tr], jr, base, q, v);
+            if (mode) tile_update<D>(rt[tr], f, mode == 2, v, sl2);
+        }
+    }
+
+    // merge the four waves' states: (2,3) -> (0,1) -> 0
+#pragma unroll
+    for (int tr = 0; tr < RT; ++tr) sum_lane_groups<D>(rt[tr]);
+    auto put = [&](int buf) {
+#pragma unroll
+        for (int tr = 0; tr < RT; ++tr) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) s_st[buf][tr][n][dt * 16 + 4 * q + jj] = rt[tr].o[dt][jj];
+            if (q == 0) {
+                s_st[buf][tr][n][D] = rt[tr].m;
+                s_st[buf][tr][n][D + 1] = rt[tr].l;
+            }
+        }
+    };
+    auto take = [&](int buf) {
+#pragma unroll
+        for (int tr = 0; tr < RT; ++tr) {
+            const float m2 = s_st[buf][tr][n][D], l2 = s_st[buf][tr][n][D + 1];
+            const float mn = fmaxf(rt[tr].m, m2);
+            const float w1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((rt[tr].m - mn) * a.scale_log2);
+            const float w2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * a.scale_log2);
+            rt[tr].m = mn;
+            rt[tr].l = rt[tr].l * w1 + l2 * w2;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    rt[tr].o[dt][jj] = rt[tr].o[dt][jj] * w1 + s_st[buf][tr][n][dt * 16 + 4 * q + jj] * w2;
+        }
+    };
+    __syncthreads();            // every wave is done with its staging tile
+    if (wave >= 2) put(wave - 2);
+    __syncthreads();
+    if (wave < 2) take(wave);
+    __syncthreads();
+    if (wave == 1) put(0);
+    __syncthreads();
+    if (wave != 0) return;
+    take(0);
+#pragma unroll
+    for (int tr = 0; tr < RT; ++tr) write_result<D>(a, s_rows, it, rt[tr], u_base + 16 * tr + n, q);
+}
+
+// ---------------------------------------------------------------- combine
+
+// Merge the chunk partials of every row-head of multi-chunk sequences:
+// M = max m_c, l = sum l_c 2^(m_c - M), O = sum O_c 2^(m_c - M) / l.
+template <int D>
+__global__ void __launch_bounds__(256) k_combine(VerifyArgs a) {
+    const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t total = (int64_t)a.B * a.Hkv * a.M;
+    if (idx >= total) return;
+    const int u = (int)(idx % a.M);
+    const int bg = (int)(idx / a.M);
+    const int g = bg % a.Hkv, b = bg / a.Hkv;
+    const int64_t L = a.lens[b];
+    const int nc_b = L > 0 ? (int)((L + a.cl - 1) / a.cl) : 1;
+    if (nc_b == 1) return;
+    const float* base = a.part + ((int64_t)bg * a.nc) * a.M * (D + 2);
+    float mx = -INFINITY;
+    for (int c = 0; c < nc_b; ++c) mx = fmaxf(mx, base[((int64_t)c * a.M + u) * (D + 2) + D]);
+    float lt = 0.f;
+    constexpr int NE = (D + 63) / 64;
+    float acc[NE];
+#pragma unroll
+    for (int t = 0; t < NE; ++t) acc[t] = 0.f;
+    for (int c = 0; c < nc_b; ++c) {
+        const float* p = base + ((int64_t)c * a.M + u) * (D + 2);
+        const float w = p[D] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(p[D] - mx);
+        lt += w * p[D + 1];
+#pragma unroll
+        for (int t = 0; t < NE; ++t) {
+            const int e = lane + 64 * t;
+            if (e < D) acc[t] += w * p[e];
+        }
+    }
+    const uint32_t rw = a.rows[u / a.group];
+    const int orig = (int)(rw >> 16), h = g * a.group + u % a.group;
+    float* op = a.out + (((int64_t)b * a.n_rows + orig) * a.Hq + h) * D;
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int t = 0; t < NE; ++t) {
+        const int e = lane + 64 * t;
+        if (e < D) op[e] = acc[t] * inv;
+    }
+    if (lane == 0) a.lse[((int64_t)b * a.n_rows + orig) * a.Hq + h] = (mx + log2f(lt)) * kLn2;
+}
+
+template <typename K>
+hipError_t launch_items(K kern, const VerifyArgs& a, hipStream_t s, int threads = 256) {
+    const int64_t slots = (int64_t)a.nrb * ((a.n_groups + 7) / 8);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * slots)), dim3(threads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int keys_max_row_tiles(int d) { return d == 128 ? 1 : 2; }
+int rows_max_row_tiles(int d) { return d == 64 ? 2 : 1; }
+
+hipError_t launch_verify_keys(const VerifyArgs& a, int rt, hipStream_t s) {
+    if (rt < 1 || rt > keys_max_row_tiles(a.d)) return hipErrorInvalidValue;
+    switch (a.d * 4 + rt) {
+        case 64 * 4 + 1: return launch_items(k_verify_keys<64, 1>, a, s);
+        case 64 * 4 + 2: return launch_items(k_verify_keys<64, 2>, a, s);
+        case 96 * 4 + 1: return launch_items(k_verify_keys<96, 1>, a, s);
+        case 96 * 4 + 2: return launch_items(k_verify_keys<96, 2>, a, s);
+        case 128 * 4 + 1: return launch_items(k_verify_keys<128, 1>, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_verify_rows(const VerifyArgs& a, int rtw, hipStream_t s) {
+    if (rtw < 1 || rtw > rows_max_row_tiles(a.d)) return hipErrorInvalidValue;
+    switch (a.d * 4 + rtw) {
+        case 64 * 4 + 1: return launch_items(k_verify_rows<64, 1>, a, s, 512);
+        case 64 * 4 + 2: return launch_items(k_verify_rows<64, 2>, a, s, 512);
+        case 96 * 4 + 1: return launch_items(k_verify_rows<96, 1>, a, s, 512);
+        case 96 * 4 + 2: return launch_items(k_verify_rows<96, 2>, a, s, 512);
+        case 128 * 4 + 1: return launch_items(k_verify_rows<128, 1>, a, s, 512);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(const VerifyArgs& a, hipStream_t s) {
+    const int64_t units = (int64_t)a.B * a.Hkv * a.M;
+    const unsigned blocks = (unsigned)((units + 3) / 4);
+    if (blocks == 0) return hipSuccess;
+    switch (a.d) {
+        case 64: hipLaunchKernelGGL(k_combine<64>, dim3(blocks), dim3(256), 0, s, a); break;
+        case 96: hipLaunchKernelGGL(k_combine<96>, dim3(blocks), dim3(256), 0, s, a); break;
+        case 128: hipLaunchKernelGGL(k_combine<128>, dim3(blocks), dim3(256), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ripe
