@@ -391,16 +391,34 @@ __device__ inline void load_stage(const uint16_t* Kt, const uint16_t* Vt, uint16
     }
 }
 
+// Workgroup barrier that waits for this wave's LDS operations but leaves its
+// global loads in flight (no memory fence, so no vmcnt(0)); the memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ inline int wave_min(int x) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) x = min(x, __shfl_xor(x, o));
+    return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ inline int wave_max(int x) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) x = max(x, __shfl_xor(x, o));
+    return __builtin_amdgcn_readfirstlane(x);
+}
+
 // Eight waves: waves w and w+4 own the same 16*RTW row-heads and take the
 // even and odd tiles of the stream (key halves kh = 0, 1), so every SIMD runs
 // two independent tile steps; their softmax states merge through LDS at the end.
+// All loop control is wave-uniform scalar code; deep tiles that every row-head
+// of a row tile reads need no masking.
 template <int D, int RTW>
 __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     constexpr int TILE = 32 * D;                 // elements of one K or V tile
     // LDS pipeline stages (one tile per half each); the workgroup's LDS stays
-    // below 128 KB
+    // well below the CU's 160 KB
     constexpr int S = D == 128 ? 3 : 4;
-    constexpr int PER_THREAD = D / 32;           // global->LDS loads per thread per tile
+    constexpr int PT = D / 32;                   // global->LDS loads per thread per tile
     constexpr int PF = D / 16;                   // prefetched draft-block pieces per lane
     constexpr int MS = D / 4 + 2;                // floats of one lane's state in the merge
     __shared__ __attribute__((aligned(16))) uint16_t s_tile[S][2][2 * TILE];
@@ -409,29 +427,35 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     static_assert(4 * RTW * 64 * MS * 4 <= (int)sizeof(s_tile), "merge buffer");
     static_assert(4 * 2 * TILE * 2 <= (int)sizeof(s_tile), "per-wave block scratch");
 
+    const int tid = threadIdx.x;
+    const uint32_t myrow = tid < a.rows_here ? a.rows[tid] : 0u;   // in flight early
     Item it;
     if (!decode_item(a, it)) return;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, n = lane & 15, q = lane >> 4;
     const int rw = wave & 3, kh = wave >> 2;     // row group, key half
-    const int n = lane & 15, q = lane >> 4;
     const int G = a.group;
     const int u_blk = it.rb * 64 * RTW;          // first row-head of the workgroup
     const int u_w = u_blk + rw * 16 * RTW;       // first row-head of this wave
-    stage_rows(a, s_rows);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        // loops r < R present in the workgroup (rows are sorted by loop): ring planes
-        const int k_lo = u_blk / G;
-        const int k_hi = min(a.rows_here, (min(a.M, u_blk + 64 * RTW) + G - 1) / G);
-        int nl = 0, prev = -1;
-        for (int k = k_lo; k < k_hi; ++k) {
-            const int r = (s_rows[k] >> 8) & 255;
-            if (r != prev && r < a.R) s_loops[nl++] = r;
-            prev = r;
-        }
-        s_nl = nl;
-        s_E = 0;
+    const float sl2 = a.scale_log2;
+    const int cl = (int)a.cl;
+    const int d0 = it.c * cl;
+    const int64_t dreg = ((int64_t)it.b * a.Hkv + it.g) * a.CP * D;
+    const uint16_t* const gK = a.deep_k + dreg;
+    const uint16_t* const gV = a.deep_v + dreg;
+
+    // every row-head reads loop R at positions [0, L - W): issue those tiles now
+    const int e_lb = (int)max((int64_t)0, min((int64_t)it.L, (int64_t)it.L - a.W));
+    const int n_early = min(d0 + cl, e_lb) > d0 ? (min(d0 + cl, e_lb) - d0 + 31) / 32 : 0;
+    for (int i = 0; i < S - 1; ++i) {
+        const int t = 2 * i + kh;
+        if (t < n_early)
+            load_stage<D>(gK + (int64_t)(d0 + 32 * t) * D, gV + (int64_t)(d0 + 32 * t) * D,
+                          s_tile[i][kh], rw, lane);
     }
+    if (tid < a.rows_here) s_rows[tid] = myrow;
+    if (tid == 0) s_E = 0;
+    lds_barrier();
 
     RowTile<D> rt[RTW];
     int e_max = 0;
@@ -440,13 +464,29 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
         init_row<D>(a, s_rows, it, u_w + 16 * t + n, q, rt[t]);
         if (RI_OK(rt[t].ri)) e_max = max(e_max, rt[t].e);
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) e_max = max(e_max, __shfl_xor(e_max, o));
-    __syncthreads();
+    e_max = wave_max(e_max);
+    // loops r < R present in the workgroup, ascending (rows are sorted by loop)
+    const int k_lo = u_blk / G;
+    const int k_hi = min(a.rows_here, (min(a.M, u_blk + 64 * RTW) + G - 1) / G);
+    if (wave == 0) {
+        int count = 0;
+        for (int k0 = k_lo; k0 < k_hi; k0 += 64) {
+            const int k = k0 + lane;
+            const int r = k < k_hi ? (int)((s_rows[k] >> 8) & 255) : -1;
+            const int rp = (k < k_hi && k > k_lo) ? (int)((s_rows[k - 1] >> 8) & 255) : -1;
+            const bool first = r >= 0 && r != rp && r < a.R;
+            const uint64_t m = __ballot(first);
+            const int pos = count + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            if (first) s_loops[pos] = r;
+            count += __popcll(m);
+        }
+        if (lane == 0) s_nl = count;
+    }
     if (lane == 0) atomicMax(&s_E, e_max);
 
     // this wave's loops (ascending) with their largest block offsets
-    int wl[2] = {-1, -1}, wimax[2] = {0, 0}, n_wl = 0;
+    int wl[2] = {0, 0}, wimax[2] = {0, 0}, n_wl = 0;
     bool wl_more = false;                         // more than two loops: slow path
     {
         int done = 0;
@@ -455,9 +495,7 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
 #pragma unroll
             for (int t = 0; t < RTW; ++t)
                 if (RI_OK(rt[t].ri) && !((done >> t) & 1)) r = min(r, (int)RI_R(rt[t].ri));
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) r = min(r, __shfl_xor(r, o));
-            r = __builtin_amdgcn_readfirstlane(r);
+            r = wave_min(r);
             if (r == 1 << 30) break;
             if (round == 2) { wl_more = true; break; }
             int im = 0;
@@ -467,10 +505,8 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
                     im = max(im, (int)RI_I(rt[t].ri));
                     done |= 1 << t;
                 }
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) im = max(im, __shfl_xor(im, o));
             wl[round] = r;
-            wimax[round] = __builtin_amdgcn_readfirstlane(im);
+            wimax[round] = wave_max(im);
             n_wl = round + 1;
         }
     }
@@ -487,57 +523,74 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
         pf[k] = make_uint4(0, 0, 0, 0);
         if (pf_ok && sl < n_wl && key < a.n_blk && key <= wimax[sl]) {
             const View& vw = kv ? a.bv : a.bk;
-            const uint16_t* src = vw.p + it.b * vw.sb + (int64_t)(wl[sl] - 1) * vw.sp +
+            const uint16_t* src = vw.p + it.b * vw.sb + (int64_t)((sl ? wl[1] : wl[0]) - 1) * vw.sp +
                                   it.g * vw.sh + key * vw.st + c8 * 8;
             pf[k] = *reinterpret_cast<const uint4*>(src);
         }
     }
-    __syncthreads();
-    const int E = s_E;
-    const int nl = s_nl;
+    lds_barrier();
+    const int E = __builtin_amdgcn_readfirstlane(s_E);
+    const int nl = __builtin_amdgcn_readfirstlane(s_nl);
+    const int loops_v0 = lane < nl ? s_loops[lane] : 0;          // loop p in lane p
+    const int loops_v1 = lane + 64 < nl ? s_loops[lane + 64] : 0;
 
-    const int d0 = (int)((int64_t)it.c * a.cl);
-    const int d1 = (int)min((int64_t)d0 + a.cl, (int64_t)E);
+    const int d1 = min(d0 + cl, E);
     const int n_deep = d1 > d0 ? (d1 - d0 + 31) / 32 : 0;
     const int ring_tiles = (it.last && a.R > 1 && it.nsl > 0) ? (it.nsl + 31) / 32 : 0;
     const int n_tiles = n_deep + nl * ring_tiles;
-    const float sl2 = a.scale_log2;
-
-    const int64_t dreg = ((int64_t)it.b * a.Hkv + it.g) * a.CP * D;
-    const int64_t rreg0 = ((int64_t)it.b * a.Hkv + it.g) * a.NR * a.WP * D;
-    // tile t of the stream: deep tiles of the chunk, then the ring tiles of each
-    // loop; iteration i holds tiles 2i (half 0) and 2i+1 (half 1)
     const int n_iter = (n_tiles + 1) / 2;
     const int n_mine = kh == 0 ? n_iter : n_tiles / 2;   // iterations with a tile for this half
-    auto issue = [&](int i) {
-        const int t = 2 * i + kh;
-        if (t >= n_tiles) return;
-        const uint16_t *Kt, *Vt;
-        if (t < n_deep) {
-            const int64_t off = dreg + (int64_t)(d0 + 32 * t) * D;
-            Kt = a.deep_k + off;
-            Vt = a.deep_v + off;
-        } else {
-            const int p = (t - n_deep) / ring_tiles, st = (t - n_deep) % ring_tiles;
-            const int64_t off = rreg0 + (int64_t)(s_loops[p] - 1) * a.WP * D + (int64_t)st * TILE;
-            Kt = a.ring_k + off;
-            Vt = a.ring_v + off;
-        }
-        load_stage<D>(Kt, Vt, s_tile[i % S][kh], rw, lane);
+    const int64_t rreg0 = ((int64_t)it.b * a.Hkv + it.g) * a.NR * a.WP * D;
+    const int WPD = (int)a.WP * D;
+
+    // per row tile: the deep positions this wave's row-heads read end at
+    // lim = min(e_row, d1); tiles below the smallest lim need no mask, tiles at
+    // or past the largest are skipped
+    int full_lim[RTW], any_lim[RTW];
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+        const int lim = min(rt[t].e, d1);
+        full_lim[t] = wave_min(RI_OK(rt[t].ri) ? lim : (1 << 30));
+        any_lim[t] = wave_max(RI_OK(rt[t].ri) ? lim : -1);
+    }
+
+    // tile t of the stream: deep tiles of the chunk, then the ring tiles of
+    // each loop; iteration i holds tiles 2i (half 0) and 2i+1 (half 1)
+    auto ring_pos = [&](int t, int& r, int& st) {
+        const int x = t - n_deep;
+        const int p = ring_tiles == 1 ? x : (ring_tiles == 2 ? x >> 1 : x / ring_tiles);
+        st = x - p * ring_tiles;
+        r = p < 64 ? __builtin_amdgcn_readlane(loops_v0, p) : __builtin_amdgcn_readlane(loops_v1, p - 64);
     };
-    for (int i = 0; i < S - 1 && i < n_iter; ++i) issue(i);
+    auto issue = [&](int t, uint16_t* stage) {
+        if (t < n_deep) {
+            const int64_t off = (int64_t)(d0 + 32 * t) * D;
+            load_stage<D>(gK + off, gV + off, stage, rw, lane);
+        } else {
+            int r, st;
+            ring_pos(t, r, st);
+            const int64_t off = rreg0 + (int64_t)(r - 1) * WPD + (int64_t)st * TILE;
+            load_stage<D>(a.ring_k + off, a.ring_v + off, stage, rw, lane);
+        }
+    };
+    for (int i = 0; i < S - 1; ++i) {
+        const int t = 2 * i + kh;
+        if (t < n_tiles && t >= n_early) issue(t, s_tile[i][kh]);
+    }
+
     for (int i = 0; i < n_iter; ++i) {
         // this thread's loads of iteration i are done when at most its loads of
         // the later issued iterations are outstanding (s_waitcnt vmcnt(N); 0xF70
         // leaves expcnt and lgkmcnt unconstrained)
         const int later = max(0, min(i + S - 2, n_mine - 1) - i);
-        if (later >= 2) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * PER_THREAD));
-        else if (later == 1) __builtin_amdgcn_s_waitcnt(0xF70 | PER_THREAD);
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * PT));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(0xF70 | PT);
         else __builtin_amdgcn_s_waitcnt(0xF70);
         // every wave's part of iteration i is in LDS, and every wave finished
         // reading stage (i-1) % S (its reads complete inside lds_frags)
-        __builtin_amdgcn_s_barrier();
-        if (i + S - 1 < n_iter) issue(i + S - 1);
+        asm volatile("s_barrier" ::: "memory");
+        const int ti = 2 * (i + S - 1) + kh;
+        if (ti < n_tiles) issue(ti, s_tile[(i + S - 1) % S][kh]);
         const int t = 2 * i + kh;
         if (t >= n_tiles) continue;
         const uint16_t* stage = s_tile[i % S][kh];
@@ -547,17 +600,23 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
             const int base = d0 + 32 * t;
 #pragma unroll
             for (int tr = 0; tr < RTW; ++tr) {
+                if (base >= any_lim[tr]) continue;
+                if (!have) lds_frags<D>(stage, f, n, q);
+                have = true;
                 bool v[8];
-                const int mode = mask_deep<D>(rt[tr], base, d1, q, v);
-                if (mode) {
-                    if (!have) lds_frags<D>(stage, f, n, q);
-                    have = true;
-                    tile_update<D>(rt[tr], f, mode == 2, v, sl2);
+                const bool full = base + 32 <= full_lim[tr];
+                if (!full) {
+                    const int lim = min(rt[tr].e, d1);
+                    const bool ok = RI_OK(rt[tr].ri);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = ok && base + key_of(e, q) < lim;
                 }
+                tile_update<D>(rt[tr], f, full, v, sl2);
             }
         } else {
-            const int p = (t - n_deep) / ring_tiles, base = ((t - n_deep) % ring_tiles) * 32;
-            const int r = s_loops[p];
+            int r, st;
+            ring_pos(t, r, st);
+            const int base = st * 32;
 #pragma unroll
             for (int tr = 0; tr < RTW; ++tr) {
                 bool v[8];
@@ -570,8 +629,9 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
         }
     }
 
-    // merge half 1 into half 0 (lane-wise: both hold the same row-heads)
-    __syncthreads();
+    // merge half 1 into half 0 (lane-wise: both hold the same row-heads); all
+    // stage loads completed in the last iterations
+    lds_barrier();
     float* s_m = reinterpret_cast<float*>(&s_tile[0][0][0]);
     if (kh == 1) {
 #pragma unroll
@@ -585,7 +645,7 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
             dst[D / 4 + 1] = rt[tr].l;
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (kh == 0) {
 #pragma unroll
         for (int tr = 0; tr < RTW; ++tr) {
@@ -602,7 +662,7 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
                 for (int j = 0; j < 4; ++j) rt[tr].o[dt][j] = rt[tr].o[dt][j] * w1 + src[dt * 4 + j] * w2;
         }
     }
-    __syncthreads();                               // merge buffer free again
+    lds_barrier();                                 // merge buffer free again
     if (kh == 1) return;
 
     if (it.last) {
@@ -611,10 +671,11 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
         // draft-block keys of the wave's loops: from the prefetched registers when
         // they fit, else staged straight from the caller's buffer
         for (int sl = 0; sl < n_wl; ++sl) {
-            const int r = wl[sl];
+            const int r = sl ? wl[1] : wl[0];
+            const int imax = sl ? wimax[1] : wimax[0];
             const uint16_t* bK = a.bk.p + it.b * a.bk.sb + (int64_t)(r - 1) * a.bk.sp + it.g * a.bk.sh;
             const uint16_t* bV = a.bv.p + it.b * a.bv.sb + (int64_t)(r - 1) * a.bv.sp + it.g * a.bv.sh;
-            for (int base = 0; base <= wimax[sl]; base += 32) {
+            for (int base = 0; base <= imax; base += 32) {
                 if (pf_ok) {
                     for (int z = lane; z < 2 * TILE / 8; z += 64)
                         *reinterpret_cast<uint4*>(sk + z * 8) = make_uint4(0, 0, 0, 0);
@@ -656,15 +717,14 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
             int done = 0;
 #pragma unroll
             for (int t = 0; t < RTW; ++t)
-                if (RI_OK(rt[t].ri) && (RI_R(rt[t].ri) == wl[0] || RI_R(rt[t].ri) == wl[1])) done |= 1 << t;
+                if (RI_OK(rt[t].ri) && ((int)RI_R(rt[t].ri) == wl[0] || (int)RI_R(rt[t].ri) == wl[1]))
+                    done |= 1 << t;
             for (;;) {
                 int r = 1 << 30;
 #pragma unroll
                 for (int t = 0; t < RTW; ++t)
                     if (RI_OK(rt[t].ri) && !((done >> t) & 1)) r = min(r, (int)RI_R(rt[t].ri));
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) r = min(r, __shfl_xor(r, o));
-                r = __builtin_amdgcn_readfirstlane(r);
+                r = wave_min(r);
                 if (r == 1 << 30) break;
                 int im = 0;
 #pragma unroll
@@ -673,9 +733,7 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
                         im = max(im, (int)RI_I(rt[t].ri));
                         done |= 1 << t;
                     }
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) im = max(im, __shfl_xor(im, o));
-                im = __builtin_amdgcn_readfirstlane(im);
+                im = wave_max(im);
                 const uint16_t* bK = a.bk.p + it.b * a.bk.sb + (int64_t)(r - 1) * a.bk.sp + it.g * a.bk.sh;
                 const uint16_t* bV = a.bv.p + it.b * a.bv.sb + (int64_t)(r - 1) * a.bv.sp + it.g * a.bv.sh;
                 for (int base = 0; base <= im; base += 32) {
