@@ -9,12 +9,14 @@ than the 256 MB Infinity Cache.  Each copy's round is captured once in a HIP
 graph; the timed loop replays the graphs between two events.
 
 Prints one JSON line: unique-KV GB/s (value), verified tokens/s, the roofline
-fraction of the verify kernel, and the fp64 oracle timed on the host cores
-on a bounded sample (one layer) of the same workload.
+of the verify launch (HBM bytes or matrix-core flops, whichever bounds the
+workload), and the fp64 oracle timed on the host cores on a bounded sample
+(whole layers) of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -25,8 +27,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "RIPE verify-attn unique-KV GB/s (% HBM peak) + verified tokens/s, L=1K–32K"
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0     # MI355X dense bf16 matrix peak
 MALL_BYTES = 256 << 20
+CPU_SAMPLE_S = 10.0             # oracle layers are timed until this much CPU time is spent
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_traffic_counters.txt")
+SPIN_CYCLES = 20_000_000        # a spinning kernel that covers the host's enqueue of timed launches
 
 
 def parse():
@@ -42,7 +48,16 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graphs")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
+
+
+def key_range(L, i, r, R, window, anchor):
+    """e_row: committed positions [0, e) are read at loop R, [e, L) at loop r."""
+    t = L + i
+    beta = t - window if anchor == 0 else L - window
+    return L if r == R else min(max(beta, 0), L)
 
 
 def unique_kv_bytes(wl, window, anchor, rows, lens):
@@ -54,36 +69,99 @@ def unique_kv_bytes(wl, window, anchor, rows, lens):
         e_max_R = 0     # committed positions [0, e_max_R) read at loop R
         blk = {}        # loop -> largest block offset read at that loop
         for i, r in rows:
-            t = L + i
-            beta = t - window if anchor == 0 else L - window
-            e = L if r == R else min(max(beta, 0), L)
+            e = key_range(L, i, r, R, window, anchor)
             e_max_R = max(e_max_R, e)
             if r < R and e < L:
                 e_min[r] = min(e_min.get(r, L), e)
             blk[r] = max(blk.get(r, -1), i)
-        n = e_max_R + sum(L - e for e in e_min.values()) + sum(i + 1 for i in blk.values())
-        total += n
+        total += e_max_R + sum(L - e for e in e_min.values()) + sum(i + 1 for i in blk.values())
     return total * 2 * H * d * 2
 
 
-def cpu_baseline(wl, window, anchor, rows):
-    """The fp64 oracle on one layer of the workload (the same rows, every head)."""
-    import numpy as np
-    import oracle
-    w = wl.replace(n_layers=1)
-    oc = oracle.prefix_cache(w, layers=[0], anchor=anchor, window=window)
-    q = w.queries(0)
+def flops(wl, rows, lens):
+    """Q.K^T plus P.V: 4*d per (row, query head, attended key)."""
+    keys = sum(L + i + 1 for L in lens for i, _ in rows)
+    return 4 * wl.head_dim * wl.n_heads_q * keys
+
+
+def src_digest():
+    """Digest of the kernel sources (ties stored counter readings to a build)."""
+    h = hashlib.sha256()
+    cdir = os.path.join(ROOT, "self_speculative_verify_amd", "csrc")
+    for name in sorted(os.listdir(cdir)):
+        with open(os.path.join(cdir, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload, digest):
+    """HBM bytes per verify launch from the committed counter summary, or None
+    when it is absent or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) >= 4 and parts[0] == "traffic" and parts[1] == workload and parts[2] == digest:
+            return int(parts[3])
+    return None
+
+
+def time_append(wl, window, anchor, dev, n_rep):
+    """ripe_append of the n_blk accepted tokens of every sequence (loop R to the
+    deep rows, loops 1..R-1 to the rings, evicting the oldest window positions),
+    one layer, n_rep appends in a row on a cache with room for them."""
+    import torch
+    import ripe_harness as H
+    w = wl.replace(n_layers=1, capacity=max(wl.lens) + wl.n_blk * (n_rep + 1))
+    cache = H.make_cache(w, device=dev, window=window, anchor=anchor)
+    H.load_prefix(cache, w, device=dev)
     bk, bv = w.block(0)
-    t0 = time.perf_counter()
-    oc.verify(0, rows, q, bk, bv, w.n_blk)
-    dt = time.perf_counter() - t0
-    u = unique_kv_bytes(w, window, anchor, rows, w.lens)
-    del np
-    return {"value": round(u / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
+    tbk, tbv = H.to_dev(bk, dev), H.to_dev(bv, dev)
+    D, R, B = w.n_blk, w.n_loops, w.batch
+    args = (tbk[:, R - 1, :, :D], tbv[:, R - 1, :, :D],
+            tbk[:, :R - 1, :, :D] if R > 1 else None, tbv[:, :R - 1, :, :D] if R > 1 else None)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SPIN_CYCLES)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
+    evs[0].record()
+    for k in range(n_rep):
+        cache.append(0, [D] * B, *args)
+        evs[k + 1].record()
+    torch.cuda.synchronize()
+    us = sum(evs[k].elapsed_time(evs[k + 1]) for k in range(n_rep)) / n_rep * 1e3
+    n_win = min(D, cache.cfg.window, w.capacity) if R > 1 else 0
+    moved = B * w.n_heads_kv * w.head_dim * 2 * 2 * (D + (R - 1) * n_win)   # K and V, bf16
+    del cache
+    return {"us_per_layer": round(us, 3), "bytes_read": moved, "bytes_written": moved,
+            "GB/s": round(2 * moved / (us * 1e-6) / 1e9, 2), "tokens_per_seq": D}
+
+
+def cpu_baseline(wl, window, anchor, rows):
+    """The fp64 oracle on whole layers of the workload (same rows, every head),
+    layer after layer until CPU_SAMPLE_S seconds are spent."""
+    import oracle
+    spent, u, n_layers = 0.0, 0, 0
+    for layer in range(wl.n_layers):
+        oc = oracle.prefix_cache(wl, layers=[layer], anchor=anchor, window=window)
+        q = wl.queries(layer)
+        bk, bv = wl.block(layer)
+        t0 = time.perf_counter()
+        oc.verify(layer, rows, q, bk, bv, wl.n_blk)
+        spent += time.perf_counter() - t0
+        u += unique_kv_bytes(wl, window, anchor, rows, wl.lens)
+        n_layers += 1
+        del oc
+        if spent >= CPU_SAMPLE_S:
+            break
+    rounds = n_layers / wl.n_layers
+    return {"value": round(u / spent / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"one of {wl.n_layers} layers: all {len(rows)} rows x {wl.n_heads_q} heads x "
-                      f"{wl.batch} sequences ({dt:.1f} s)",
-            "tokens_per_s": round(wl.batch * len({i for i, _ in rows}) / (dt * wl.n_layers), 3)}
+            "sample": f"{n_layers} of {wl.n_layers} layers: all {len(rows)} rows x {wl.n_heads_q} "
+                      f"heads x {wl.batch} sequences, {spent:.1f} s",
+            "tokens_per_s": round(wl.batch * len({i for i, _ in rows}) * rounds / spent, 3)}
 
 
 def main():
@@ -93,7 +171,6 @@ def main():
               "(the verification path is data-parallel over sequences and KV heads and "
               "needs no collective; run one process per GPU).", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     import ripe_harness as H
     from synth import WINDOW_FULL, named_workload
@@ -105,9 +182,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    u_layer = [unique_kv_bytes(wl, window, anchor, rows, wl.lens) for _ in range(wl.n_layers)]
-    u_round = sum(u_layer)
+    u_layer = unique_kv_bytes(wl, window, anchor, rows, wl.lens)
+    f_layer = flops(wl, rows, wl.lens)
+    u_round = u_layer * wl.n_layers
     copies = args.copies or max(2, 1 + math.ceil(2 * MALL_BYTES / max(u_round, 1)))
+    print(f"bench: {wl.name} W={window} anchor={anchor} copies={copies}", file=sys.stderr, flush=True)
 
     # build the caches (same contents in every copy; host data generated once)
     memo = {}
@@ -128,13 +207,18 @@ def main():
                  torch.empty((wl.batch, len(rows), wl.n_heads_q), device=dev))
                 for _ in range(wl.n_layers)]
         setups.append((cache, ins, outs))
+    memo.clear()
+    wl.prefix = orig_prefix
     torch.cuda.synchronize()
 
-    def run_round(setup):
+    def run_layer(setup, layer):
         cache, ins, outs = setup
+        q, bk, bv = ins[layer]
+        cache.verify(layer, rows, q, bk, bv, wl.n_blk, out=outs[layer][0], lse=outs[layer][1])
+
+    def run_round(setup):
         for layer in range(wl.n_layers):
-            q, bk, bv = ins[layer]
-            cache.verify(layer, rows, q, bk, bv, wl.n_blk, out=outs[layer][0], lse=outs[layer][1])
+            run_layer(setup, layer)
 
     for s in setups:            # eager warm-up (allocates workspaces outside capture)
         run_round(s)
@@ -165,10 +249,51 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / max(args.steps, 1)
     t = ms / 1e3
+
+    # per-launch duration of ripe_verify_attn: events between launches queued
+    # behind a spinning kernel, so no host gap falls between them
+    n_rep = max(1, min(args.steps, 20))
+    launch_ms = []
+    for k in range(n_rep):
+        torch.cuda._sleep(SPIN_CYCLES)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(wl.n_layers + 1)]
+        s = setups[k % copies]
+        evs[0].record()
+        for layer in range(wl.n_layers):
+            run_layer(s, layer)
+            evs[layer + 1].record()
+        torch.cuda.synchronize()
+        launch_ms += [evs[j].elapsed_time(evs[j + 1]) for j in range(wl.n_layers)]
+    launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    del setups, graphs
+    append = time_append(wl, window, anchor, dev, n_rep)
+
+    if args.copy_calib:
+        n = args.copy_calib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     n_verified = wl.batch * len({i for i, _ in rows})   # draft positions verified per step
     gbs = u_round / t / 1e9
-    launch_s = t / wl.n_layers        # one verify launch per layer per step
-    achieved = (u_round / wl.n_layers) / launch_s / 1e9
+    hbm_time = u_layer / (HBM_PEAK_GBS * 1e9)
+    mfma_time = f_layer / (MFMA_BF16_PEAK_TFS * 1e12)
+    digest = src_digest()
+    traffic = stored_traffic(args.workload, digest) if window == wl.window and anchor == wl.anchor else None
+    if hbm_time >= mfma_time:
+        roof = {"bound": "hbm", "achieved": round(u_layer / launch_s / 1e9, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(f_layer / launch_s / 1e12, 2),
+                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = traffic
+    roof["launch_us"] = round(launch_s * 1e6, 3)
+    roof["algorithmic_bytes"] = u_layer
+    roof["algorithmic_flops"] = f_layer
 
     cpu = None
     if not args.no_cpu:
@@ -188,12 +313,12 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(n_verified / t, 1),
         "unique_kv_bytes_per_step": u_round,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+        "flops_per_step": f_layer * wl.n_layers,
+        "kernel_sources": digest,
+        "roofline": roof,
+        "append": append,
         "cpu_baseline": cpu,
     }
-    del np
     print(json.dumps(res), flush=True)
 
 

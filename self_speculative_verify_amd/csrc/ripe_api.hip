@@ -97,13 +97,15 @@ int env_int(const char* name, int fallback) {
 
 Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here) {
     // tuning and test overrides: workgroup target, row tiles, kernel (1 keys, 2 rows)
-    const int target = env_int("RIPE_ITEMS_TARGET", 512);
+    const int target_env = env_int("RIPE_ITEMS_TARGET", 0);
+    const int target = target_env ? target_env : 512;
     const int force_rt = env_int("RIPE_ROW_TILES", 0);
     const int force_kernel = env_int("RIPE_KERNEL", 0);
     const int force_min_chunk = env_int("RIPE_MIN_CHUNK", 0);
     Plan p;
     p.M = rows_here * (g.Hq / g.Hkv);
-    p.rows_kernel = force_kernel ? force_kernel == 2 : p.M >= 64;
+    // the rows kernel pays off once a KV head carries several hundred row-heads
+    p.rows_kernel = force_kernel ? force_kernel == 2 : p.M >= 512;
     const int64_t heads = (int64_t)g.B * g.Hkv;
     int rows_per_item;
     if (p.rows_kernel) {
@@ -122,7 +124,9 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here) {
     for (int b = 0; b < g.B; ++b) lmax = std::max<int64_t>(lmax, lens[b]);
     const int64_t base = heads * p.nrb;
     int64_t nc = 1;
-    if (base < target) {
+    // split the committed positions only when the row blocks alone leave most
+    // compute units idle; then aim for `target` workgroups
+    if (base < target && (target_env || base < 256)) {
         const int64_t min_chunk = force_min_chunk ? force_min_chunk : std::max<int64_t>(256, 8 * rows_per_item);
         nc = std::max<int64_t>(1, std::min<int64_t>((target + base - 1) / base, lmax / min_chunk));
     }
