@@ -124,9 +124,9 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here) {
     for (int b = 0; b < g.B; ++b) lmax = std::max<int64_t>(lmax, lens[b]);
     const int64_t base = heads * p.nrb;
     int64_t nc = 1;
-    // split the committed positions only when the row blocks alone leave most
-    // compute units idle; then aim for `target` workgroups
-    if (base < target && (target_env || base < 256)) {
+    // split the committed positions only when the row blocks alone leave a
+    // quarter of the compute units idle; then aim for `target` workgroups
+    if (base < target && (target_env || base < 192)) {
         const int64_t min_chunk = force_min_chunk ? force_min_chunk : std::max<int64_t>(256, 8 * rows_per_item);
         nc = std::max<int64_t>(1, std::min<int64_t>((target + base - 1) / base, lmax / min_chunk));
     }

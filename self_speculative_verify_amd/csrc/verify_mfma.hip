@@ -213,7 +213,107 @@ __device__ inline void tile_update(RowTile<D>& rt, const Frags<D>& f, bool full,
     }
 }
 
-// ---------------------------------------------------------------- item
+// S^T = K.Q^T of one key tile against one row tile: lane n, register e holds
+// the raw score of key key_of(e, q) for row-head n
+template <int D>
+__device__ inline void tile_scores(const RowTile<D>& rt, const Frags<D>& f, float (&x)[8]) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+        s0 = mfma(f.k[k][0], rt.q[k], s0);
+        s1 = mfma(f.k[k][1], rt.q[k], s1);
+    }
+    x[0] = s0[0]; x[1] = s0[1]; x[2] = s0[2]; x[3] = s0[3];
+    x[4] = s1[0]; x[5] = s1[1]; x[6] = s1[2]; x[7] = s1[3];
+}
+
+// The rest of tile_update for a key tile every row-head of the row tile reads
+// in full: no masks, every score finite, and the rescale of l and O (with its
+// exponential) only when some row-head's max moved.  Uses only f.v.
+template <int D>
+__device__ inline void tile_finish_full(RowTile<D>& rt, const Frags<D>& f, const float (&x)[8], float c) {
+    float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    bm = max_lane_groups(bm);
+    const float mo = rt.m;
+    const float mn = fmaxf(mo, bm);
+    const float nmc = -mn * c;
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c, nmc));
+        ps += p[e];
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+        hi[e2] = pack_bf16(p[2 * e2], p[2 * e2 + 1]);
+        const float h0 = __uint_as_float(hi[e2] << 16), h1 = __uint_as_float(hi[e2] & 0xffff0000u);
+        lo[e2] = pack_bf16(p[2 * e2] - h0, p[2 * e2 + 1] - h1);
+    }
+    if (__any(mo != mn)) {
+        // 2^((mo - mn) c): 0 on the first tile (mo = -inf), exactly 1 where the max stayed
+        const float alpha = __builtin_amdgcn_exp2f((mo - mn) * c);
+        rt.l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            rt.o[dt][0] *= alpha; rt.o[dt][1] *= alpha;
+            rt.o[dt][2] *= alpha; rt.o[dt][3] *= alpha;
+        }
+    }
+    rt.m = mn;
+    rt.l += ps;
+    const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) rt.o[dt] = mfma(f.v[dt], phi, rt.o[dt]);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) rt.o[dt] = mfma(f.v[dt], plo, rt.o[dt]);
+}
+
+// the rest of tile_update with masks (invalid keys get -inf); uses only f.v
+template <int D>
+__device__ inline void tile_finish_masked(RowTile<D>& rt, const Frags<D>& f, float (&x)[8],
+                                          const bool (&valid)[8], float c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = valid[e] ? x[e] : -INFINITY;
+    float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    bm = max_lane_groups(bm);
+    const float mo = rt.m;
+    const float mn = fmaxf(mo, bm);
+    const float ms = mn == -INFINITY ? 0.f : mn;     // finite reference for the exponents
+    const float nmc = -ms * c;
+    const float alpha = __builtin_amdgcn_exp2f((mo - ms) * c);
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c, nmc));
+        ps += p[e];
+    }
+    rt.m = mn;
+    rt.l = fmaf(rt.l, alpha, ps);
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+        hi[e2] = pack_bf16(p[2 * e2], p[2 * e2 + 1]);
+        const float h0 = __uint_as_float(hi[e2] << 16), h1 = __uint_as_float(hi[e2] & 0xffff0000u);
+        lo[e2] = pack_bf16(p[2 * e2] - h0, p[2 * e2 + 1] - h1);
+    }
+    const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    if (__any(mo != mn)) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            rt.o[dt][0] *= alpha; rt.o[dt][1] *= alpha;
+            rt.o[dt][2] *= alpha; rt.o[dt][3] *= alpha;
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) rt.o[dt] = mfma(f.v[dt], phi, rt.o[dt]);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) rt.o[dt] = mfma(f.v[dt], plo, rt.o[dt]);
+}
+
+// ---------------------------------------------------------------- item// ---------------------------------------------------------------- item
 
 struct Item {
     int b, g, c, rb, nc_b;
@@ -255,11 +355,12 @@ __device__ inline void stage_rows(const VerifyArgs& a, uint32_t* s_rows) {
     for (int k = threadIdx.x; k < a.rows_here; k += blockDim.x) s_rows[k] = a.rows[k];
 }
 
+// state of row-head u (query row word `rw`, see VerifyArgs::rows); row-heads
+// past M are padding (zero query, never written)
 template <int D>
-__device__ inline void init_row(const VerifyArgs& a, const uint32_t* s_rows, const Item& it, int u,
-                                int q, RowTile<D>& rt) {
+__device__ inline void init_row_word(const VerifyArgs& a, const Item& it, int u, uint32_t rw, int q,
+                                     RowTile<D>& rt) {
     const bool ok = u < a.M;
-    const uint32_t rw = s_rows[ok ? u / a.group : 0];
     const int ii = rw & 255, rr = (rw >> 8) & 255;
     rt.ri = ii | (rr << 8) | (ok ? 1 << 16 : 0);
     rt.e = e_row(a, it.L, ii, rr);
@@ -272,6 +373,11 @@ __device__ inline void init_row(const VerifyArgs& a, const uint32_t* s_rows, con
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
         rt.q[c] = ok ? *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * q) : make_uint4(0, 0, 0, 0);
+}
+template <int D>
+__device__ inline void init_row(const VerifyArgs& a, const uint32_t* s_rows, const Item& it, int u,
+                                int q, RowTile<D>& rt) {
+    init_row_word<D>(a, it, u, s_rows[u < a.M ? u / a.group : 0], q, rt);
 }
 
 // masks of one row tile against a deep / ring / block tile; false = the tile
@@ -335,10 +441,9 @@ __device__ inline void stage_block(const VerifyArgs& a, const uint16_t* K, const
 // final (single chunk) or partial (multi-chunk) result of one row tile whose
 // l is already summed over the lane groups
 template <int D>
-__device__ inline void write_result(const VerifyArgs& a, const uint32_t* s_rows, const Item& it,
-                                    const RowTile<D>& rt, int u, int q) {
+__device__ inline void write_result_word(const VerifyArgs& a, const Item& it, const RowTile<D>& rt,
+                                         int u, uint32_t rw, int q) {
     if (!RI_OK(rt.ri)) return;
-    const uint32_t rw = s_rows[u / a.group];
     const int orig = (int)(rw >> 16), h = it.g * a.group + u % a.group;
     if (it.nc_b == 1) {
         const float inv = 1.f / rt.l;
@@ -360,6 +465,12 @@ __device__ inline void write_result(const VerifyArgs& a, const uint32_t* s_rows,
         // partial max in the log2 domain (-inf stays -inf)
         if (q == 0) *reinterpret_cast<float2*>(po + D) = make_float2(rt.m * a.scale_log2, rt.l);
     }
+}
+template <int D>
+__device__ inline void write_result(const VerifyArgs& a, const uint32_t* s_rows, const Item& it,
+                                    const RowTile<D>& rt, int u, int q) {
+    if (!RI_OK(rt.ri)) return;
+    write_result_word<D>(a, it, rt, u, s_rows[u / a.group], q);
 }
 
 template <int D>
@@ -396,46 +507,110 @@ __device__ inline void load_stage(const uint16_t* Kt, const uint16_t* Vt, uint16
 // keeps the compiler from moving memory accesses across it.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ inline int wave_min(int x) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) x = min(x, __shfl_xor(x, o));
+// Wave-wide min / max: rotations within each 16-lane row (DPP row_ror), then
+// across the four rows (permlane swaps); every lane ends with the result.
+template <bool kMax>
+__device__ inline int wave_reduce(int x) {
+    auto op = [](int u, int v) { return kMax ? max(u, v) : min(u, v); };
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xf, 0xf, false));   // row_ror:8
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xf, 0xf, false));   // row_ror:4
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x122, 0xf, 0xf, false));   // row_ror:2
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x121, 0xf, 0xf, false));   // row_ror:1
+    const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    x = op((int)a[0], (int)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    x = op((int)b[0], (int)b[1]);
     return __builtin_amdgcn_readfirstlane(x);
 }
-__device__ inline int wave_max(int x) {
+__device__ inline int wave_min(int x) { return wave_reduce<false>(x); }
+__device__ inline int wave_max(int x) { return wave_reduce<true>(x); }
+
+// Direct global->LDS load of 16 bytes per lane (lane l lands at lds + 16 l),
+// written as asm so that the compiler does not treat later LDS accesses as
+// possibly aliasing an outstanding load (it would wait for every load in
+// flight); the caller waits with explicit s_waitcnt vmcnt.  No register is
+// written.
+__device__ inline void dma16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(lds) : "memory");
+}
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// load_stage through dma16
+template <int D>
+__device__ inline void load_stage_asm(const uint16_t* Kt, const uint16_t* Vt, uint16_t* stage, int wave,
+                                      int lane) {
+    constexpr int BLOCKS = D / 8;
+    static_assert(BLOCKS % 4 == 0, "four waves share the blocks");
+    const int src_off = (lane & 15) * 32 + (lane >> 4) * 8;
+    const uint32_t base = lds_addr(stage);
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) x = max(x, __shfl_xor(x, o));
-    return __builtin_amdgcn_readfirstlane(x);
+    for (int j = 0; j < BLOCKS / 4; ++j) {
+        const int blk = j * 4 + wave;
+        const uint16_t* src = (blk < BLOCKS / 2 ? Kt + blk * 512 : Vt + (blk - BLOCKS / 2) * 512) + src_off;
+        dma16(src, base + blk * 1024);
+    }
+}
+// The operand pieces of a staged tile pair as ordinary LDS loads (piece i at
+// stage + 1 KB * i, this lane's 16 bytes at + 16 lane): the key half and the
+// value half separately.
+template <int D>
+__device__ inline void lds_keys(const uint16_t* stage, Frags<D>& f, int lane) {
+    const uint4* p = reinterpret_cast<const uint4*>(stage) + lane;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+        f.k[c][0] = p[(2 * c) * 64];
+        f.k[c][1] = p[(2 * c + 1) * 64];
+    }
+}
+template <int D>
+__device__ inline void lds_values(const uint16_t* stage, Frags<D>& f, int lane) {
+    const uint4* p = reinterpret_cast<const uint4*>(stage) + lane;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = p[(D / 16 + dt) * 64];
 }
 
 // Eight waves: waves w and w+4 own the same 16*RTW row-heads and take the
 // even and odd tiles of the stream (key halves kh = 0, 1), so every SIMD runs
 // two independent tile steps; their softmax states merge through LDS at the end.
-// All loop control is wave-uniform scalar code; deep tiles that every row-head
-// of a row tile reads need no masking.
+// The stream is the chunk's deep tiles, then the ring tiles of every loop
+// r < R present in the workgroup.  All eight waves load each tile pair into an
+// LDS stage with direct global->LDS loads, S - 1 iterations ahead, and read it
+// with asm LDS reads.  Row data goes from the kernel arguments into registers,
+// and compiler-visible code touches no LDS between the first direct load and
+// the merge, so the compiler never drains the load pipeline; all waits on the
+// direct loads are explicit.  Deep tiles that every row-head reads in full take
+// the unmasked step.
 template <int D, int RTW>
 __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     constexpr int TILE = 32 * D;                 // elements of one K or V tile
-    // LDS pipeline stages (one tile per half each); the workgroup's LDS stays
-    // well below the CU's 160 KB
-    constexpr int S = D == 128 ? 3 : 4;
-    constexpr int PT = D / 32;                   // global->LDS loads per thread per tile
+    // LDS pipeline stages (one tile pair per half each): 128 / 144 / 128 KB
+    constexpr int S = D == 128 ? 4 : (D == 96 ? 6 : 8);
+    constexpr int PT = D / 32;                   // direct loads per thread per tile pair
     constexpr int PF = D / 16;                   // prefetched draft-block pieces per lane
     constexpr int MS = D / 4 + 2;                // floats of one lane's state in the merge
     __shared__ __attribute__((aligned(16))) uint16_t s_tile[S][2][2 * TILE];
-    __shared__ uint32_t s_rows[kMaxRowsPerLaunch];
-    __shared__ int s_E, s_nl, s_loops[kMaxRowsPerLaunch];
+    __shared__ __attribute__((aligned(16))) uint4 s_q[4][RTW * (D / 32)][64];   // query operands per row group
     static_assert(4 * RTW * 64 * MS * 4 <= (int)sizeof(s_tile), "merge buffer");
     static_assert(4 * 2 * TILE * 2 <= (int)sizeof(s_tile), "per-wave block scratch");
+    static_assert(RTW <= 2, "two row words per lane");
 
     const int tid = threadIdx.x;
-    const uint32_t myrow = tid < a.rows_here ? a.rows[tid] : 0u;   // in flight early
-    Item it;
-    if (!decode_item(a, it)) return;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, n = lane & 15, q = lane >> 4;
     const int rw = wave & 3, kh = wave >> 2;     // row group, key half
     const int G = a.group;
-    const int u_blk = it.rb * 64 * RTW;          // first row-head of the workgroup
+    // the workgroup's rows k_lo .. k_lo+nk-1 (sorted by loop, then block
+    // offset), loaded first since they do not depend on the sequence: row
+    // k_lo + lane in w0, row k_lo + 64 + lane in w1
+    const int u_blk = (int)((blockIdx.x >> 3) % a.nrb) * 64 * RTW;   // first row-head of the workgroup
+    const int k_lo = u_blk / G;
+    const int nk = min(a.rows_here, (min(a.M, u_blk + 64 * RTW) + G - 1) / G) - k_lo;
+    const uint32_t w0 = lane < nk ? a.rows[k_lo + lane] : 0u;
+    const uint32_t w1 = lane + 64 < nk ? a.rows[k_lo + 64 + lane] : 0u;
+
+    Item it;
+    if (!decode_item(a, it)) return;
     const int u_w = u_blk + rw * 16 * RTW;       // first row-head of this wave
     const float sl2 = a.scale_log2;
     const int cl = (int)a.cl;
@@ -443,109 +618,84 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     const int64_t dreg = ((int64_t)it.b * a.Hkv + it.g) * a.CP * D;
     const uint16_t* const gK = a.deep_k + dreg;
     const uint16_t* const gV = a.deep_v + dreg;
-
-    // every row-head reads loop R at positions [0, L - W): issue those tiles now
-    const int e_lb = (int)max((int64_t)0, min((int64_t)it.L, (int64_t)it.L - a.W));
-    const int n_early = min(d0 + cl, e_lb) > d0 ? (min(d0 + cl, e_lb) - d0 + 31) / 32 : 0;
-    for (int i = 0; i < S - 1; ++i) {
-        const int t = 2 * i + kh;
-        if (t < n_early)
-            load_stage<D>(gK + (int64_t)(d0 + 32 * t) * D, gV + (int64_t)(d0 + 32 * t) * D,
-                          s_tile[i][kh], rw, lane);
-    }
-    if (tid < a.rows_here) s_rows[tid] = myrow;
-    if (tid == 0) s_E = 0;
-    lds_barrier();
+    auto row_at = [&](int k) -> uint32_t {       // row word k (wave-uniform k < nk)
+        return k < 64 ? (uint32_t)__builtin_amdgcn_readlane(w0, k) : (uint32_t)__builtin_amdgcn_readlane(w1, k - 64);
+    };
 
     RowTile<D> rt[RTW];
-    int e_max = 0;
+    uint32_t rword[RTW];
 #pragma unroll
     for (int t = 0; t < RTW; ++t) {
-        init_row<D>(a, s_rows, it, u_w + 16 * t + n, q, rt[t]);
-        if (RI_OK(rt[t].ri)) e_max = max(e_max, rt[t].e);
+        const int u = u_w + 16 * t + n;
+        const int k = (u < a.M ? u / G : k_lo) - k_lo;
+        const uint32_t x0 = __shfl(w0, k & 63), x1 = __shfl(w1, k & 63);
+        rword[t] = k < 64 ? x0 : x1;
+        const bool ok = u < a.M;
+        const int ii = rword[t] & 255, rr = (rword[t] >> 8) & 255;
+        rt[t].ri = ii | (rr << 8) | (ok ? 1 << 16 : 0);
+        rt[t].e = e_row(a, it.L, ii, rr);
+        rt[t].m = -INFINITY;
+        rt[t].l = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) rt[t].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    e_max = wave_max(e_max);
-    // loops r < R present in the workgroup, ascending (rows are sorted by loop)
-    const int k_lo = u_blk / G;
-    const int k_hi = min(a.rows_here, (min(a.M, u_blk + 64 * RTW) + G - 1) / G);
-    if (wave == 0) {
-        int count = 0;
-        for (int k0 = k_lo; k0 < k_hi; k0 += 64) {
-            const int k = k0 + lane;
-            const int r = k < k_hi ? (int)((s_rows[k] >> 8) & 255) : -1;
-            const int rp = (k < k_hi && k > k_lo) ? (int)((s_rows[k - 1] >> 8) & 255) : -1;
-            const bool first = r >= 0 && r != rp && r < a.R;
-            const uint64_t m = __ballot(first);
-            const int pos = count + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-            if (first) s_loops[pos] = r;
-            count += __popcll(m);
+    // query operands into LDS by direct loads (waves of key half 0 load their
+    // row group's, both halves read them after the first barrier); padding
+    // row-heads load a valid query, their results are never written
+    if (kh == 0) {
+        const uint32_t qbase = lds_addr(&s_q[rw][0][0]);
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) {
+            const int u = u_w + 16 * t + n;
+            const int h = it.g * G + (u < a.M ? u % G : 0);
+            const uint16_t* qp = a.q + (((int64_t)it.b * a.n_rows + (int)(rword[t] >> 16)) * a.Hq + h) * D + 8 * q;
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c) dma16(qp + 32 * c, qbase + (t * (D / 32) + c) * 1024);
         }
-        if (lane == 0) s_nl = count;
     }
-    if (lane == 0) atomicMax(&s_E, e_max);
-
-    // this wave's loops (ascending) with their largest block offsets
-    int wl[2] = {0, 0}, wimax[2] = {0, 0}, n_wl = 0;
-    bool wl_more = false;                         // more than two loops: slow path
+    // deep extent of the workgroup: the largest e_row of its rows
+    int e_here = lane < nk ? e_row(a, it.L, w0 & 255, (w0 >> 8) & 255) : 0;
+    if (lane + 64 < nk) e_here = max(e_here, e_row(a, it.L, w1 & 255, (w1 >> 8) & 255));
+    const int E = wave_max(e_here);
+    // loops r < R present in the workgroup, ascending: the p-th in lane p of
+    // loops_v0 (p < 64) or lane p - 64 of loops_v1
+    int loops_v0 = 0, loops_v1 = 0, nl = 0;
     {
-        int done = 0;
-        for (int round = 0; round < 3; ++round) {
-            int r = 1 << 30;
-#pragma unroll
-            for (int t = 0; t < RTW; ++t)
-                if (RI_OK(rt[t].ri) && !((done >> t) & 1)) r = min(r, (int)RI_R(rt[t].ri));
-            r = wave_min(r);
-            if (r == 1 << 30) break;
-            if (round == 2) { wl_more = true; break; }
-            int im = 0;
-#pragma unroll
-            for (int t = 0; t < RTW; ++t)
-                if (RI_OK(rt[t].ri) && RI_R(rt[t].ri) == r) {
-                    im = max(im, (int)RI_I(rt[t].ri));
-                    done |= 1 << t;
-                }
-            wl[round] = r;
-            wimax[round] = wave_max(im);
-            n_wl = round + 1;
+        const int r0 = (w0 >> 8) & 255, r1 = (w1 >> 8) & 255;
+        const int r0p = __shfl(r0, (lane + 63) & 63), r1p = __shfl(r1, (lane + 63) & 63);
+        const int r0_last = __builtin_amdgcn_readlane(r0, 63);
+        const bool f0 = lane < nk && r0 < a.R && (lane == 0 || r0 != r0p);
+        const bool f1 = lane + 64 < nk && r1 < a.R && r1 != (lane == 0 ? r0_last : r1p);
+        uint64_t m = __ballot(f0);
+        while (m) {
+            const int k = __builtin_ctzll(m);
+            m &= m - 1;
+            const int r = __builtin_amdgcn_readlane(r0, k);
+            loops_v0 = lane == nl ? r : loops_v0;
+            ++nl;
+        }
+        m = __ballot(f1);
+        while (m) {
+            const int k = __builtin_ctzll(m);
+            m &= m - 1;
+            const int r = __builtin_amdgcn_readlane(r1, k);
+            if (nl < 64) loops_v0 = lane == nl ? r : loops_v0;
+            else loops_v1 = lane == nl - 64 ? r : loops_v1;
+            ++nl;
         }
     }
-    // prefetch the draft-block rows of up to two loops (keys < 8) into registers;
-    // piece pc = ((slot*2 + kv)*8 + key)*(D/8) + chunk, lane holds pc = lane + 64k
-    const bool pf_ok = kh == 0 && it.last && !wl_more && (n_wl < 1 || wimax[0] < 8) &&
-                       (n_wl < 2 || wimax[1] < 8);
-    uint4 pf[PF];
-#pragma unroll
-    for (int k = 0; k < PF; ++k) {
-        const int pc = lane + 64 * k;
-        const int c8 = pc % (D / 8), rest = pc / (D / 8);
-        const int key = rest % 8, kv = (rest / 8) % 2, sl = rest / 16;
-        pf[k] = make_uint4(0, 0, 0, 0);
-        if (pf_ok && sl < n_wl && key < a.n_blk && key <= wimax[sl]) {
-            const View& vw = kv ? a.bv : a.bk;
-            const uint16_t* src = vw.p + it.b * vw.sb + (int64_t)((sl ? wl[1] : wl[0]) - 1) * vw.sp +
-                                  it.g * vw.sh + key * vw.st + c8 * 8;
-            pf[k] = *reinterpret_cast<const uint4*>(src);
-        }
-    }
-    lds_barrier();
-    const int E = __builtin_amdgcn_readfirstlane(s_E);
-    const int nl = __builtin_amdgcn_readfirstlane(s_nl);
-    const int loops_v0 = lane < nl ? s_loops[lane] : 0;          // loop p in lane p
-    const int loops_v1 = lane + 64 < nl ? s_loops[lane + 64] : 0;
 
     const int d1 = min(d0 + cl, E);
     const int n_deep = d1 > d0 ? (d1 - d0 + 31) / 32 : 0;
     const int ring_tiles = (it.last && a.R > 1 && it.nsl > 0) ? (it.nsl + 31) / 32 : 0;
     const int n_tiles = n_deep + nl * ring_tiles;
     const int n_iter = (n_tiles + 1) / 2;
-    const int n_mine = kh == 0 ? n_iter : n_tiles / 2;   // iterations with a tile for this half
     const int64_t rreg0 = ((int64_t)it.b * a.Hkv + it.g) * a.NR * a.WP * D;
-    const int WPD = (int)a.WP * D;
+    const int64_t WPD = a.WP * D;
 
     // per row tile: the deep positions this wave's row-heads read end at
     // lim = min(e_row, d1); tiles below the smallest lim need no mask, tiles at
-    // or past the largest are skipped
+    // or past the largest are skipped.  Tiles below L - W are full for everyone.
     int full_lim[RTW], any_lim[RTW];
 #pragma unroll
     for (int t = 0; t < RTW; ++t) {
@@ -553,84 +703,203 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
         full_lim[t] = wave_min(RI_OK(rt[t].ri) ? lim : (1 << 30));
         any_lim[t] = wave_max(RI_OK(rt[t].ri) ? lim : -1);
     }
+    const int e_lb = (int)max((int64_t)0, min((int64_t)it.L, (int64_t)it.L - a.W));
+    const int n_full = min(e_lb, d1) > d0 ? (min(e_lb, d1) - d0) / 32 : 0;
+    const int n_fast = min(n_iter, n_full / 2);
 
-    // tile t of the stream: deep tiles of the chunk, then the ring tiles of
-    // each loop; iteration i holds tiles 2i (half 0) and 2i+1 (half 1)
-    auto ring_pos = [&](int t, int& r, int& st) {
-        const int x = t - n_deep;
-        const int p = ring_tiles == 1 ? x : (ring_tiles == 2 ? x >> 1 : x / ring_tiles);
-        st = x - p * ring_tiles;
-        r = p < 64 ? __builtin_amdgcn_readlane(loops_v0, p) : __builtin_amdgcn_readlane(loops_v1, p - 64);
-    };
-    auto issue = [&](int t, uint16_t* stage) {
-        if (t < n_deep) {
-            const int64_t off = (int64_t)(d0 + 32 * t) * D;
-            load_stage<D>(gK + off, gV + off, stage, rw, lane);
+    // issue cursor: the j-th issue of this wave loads tile 2j + kh of the stream
+    int ti = kh, ipl = 0, ist = 0;
+    const uint16_t* iK = gK + (int64_t)(d0 + 32 * kh) * D;
+    const uint16_t* iV = gV + (int64_t)(d0 + 32 * kh) * D;
+    int issued = 0;                               // tile pairs issued by this wave
+    auto issue_next = [&](uint16_t* stage) {
+        if (ti < n_deep) {
+            load_stage_asm<D>(iK, iV, stage, rw, lane);
         } else {
-            int r, st;
-            ring_pos(t, r, st);
-            const int64_t off = rreg0 + (int64_t)(r - 1) * WPD + (int64_t)st * TILE;
-            load_stage<D>(a.ring_k + off, a.ring_v + off, stage, rw, lane);
+            if (ti - 2 < n_deep) { ipl = 0; ist = ti - n_deep; }   // first ring tile of this half
+            while (ist >= ring_tiles) { ist -= ring_tiles; ++ipl; }
+            const int r = ipl < 64 ? __builtin_amdgcn_readlane(loops_v0, ipl)
+                                   : __builtin_amdgcn_readlane(loops_v1, ipl - 64);
+            const int64_t off = rreg0 + (int64_t)(r - 1) * WPD + (int64_t)ist * TILE;
+            load_stage_asm<D>(a.ring_k + off, a.ring_v + off, stage, rw, lane);
+            ist += 2;
         }
+        ti += 2;
+        iK += 2 * TILE;
+        iV += 2 * TILE;
+        ++issued;
     };
-    for (int i = 0; i < S - 1; ++i) {
-        const int t = 2 * i + kh;
-        if (t < n_tiles && t >= n_early) issue(t, s_tile[i][kh]);
-    }
-
-    for (int i = 0; i < n_iter; ++i) {
-        // this thread's loads of iteration i are done when at most its loads of
-        // the later issued iterations are outstanding (s_waitcnt vmcnt(N); 0xF70
-        // leaves expcnt and lgkmcnt unconstrained)
-        const int later = max(0, min(i + S - 2, n_mine - 1) - i);
-        if (later >= 2) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * PT));
+    // wait until tile j of this half is in LDS: this wave's loads of it are
+    // done when at most the tiles it issued later are outstanding (s_waitcnt
+    // vmcnt(N); 0xF70 leaves expcnt and lgkmcnt unconstrained); after the
+    // barrier every wave's part is there
+    auto wait_tile = [&](int j) {
+        const int later = issued - j - 1;
+        if (later >= 5) __builtin_amdgcn_s_waitcnt(0xF70 | (5 * PT));
+        else if (later == 4) __builtin_amdgcn_s_waitcnt(0xF70 | (4 * PT));
+        else if (later == 3) __builtin_amdgcn_s_waitcnt(0xF70 | (3 * PT));
+        else if (later == 2) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * PT));
         else if (later == 1) __builtin_amdgcn_s_waitcnt(0xF70 | PT);
         else __builtin_amdgcn_s_waitcnt(0xF70);
-        // every wave's part of iteration i is in LDS, and every wave finished
-        // reading stage (i-1) % S (its reads complete inside lds_frags)
         asm volatile("s_barrier" ::: "memory");
-        const int ti = 2 * (i + S - 1) + kh;
-        if (ti < n_tiles) issue(ti, s_tile[(i + S - 1) % S][kh]);
-        const int t = 2 * i + kh;
-        if (t >= n_tiles) continue;
-        const uint16_t* stage = s_tile[i % S][kh];
-        Frags<D> f;
-        bool have = false;
-        if (t < n_deep) {
-            const int base = d0 + 32 * t;
+    };
+    static_assert(5 * 4 <= 63, "vmcnt field");
+
+    // the first S - 1 tile pairs of this half (after the query loads, so the
+    // wait for tile 0 covers them)
+    for (int j = 0; j < S - 1; ++j)
+        if (ti < n_tiles) issue_next(s_tile[j][kh]);
+
+    // this wave's loops (ascending, at most two on the fast path) with their
+    // largest block offsets, from the sorted row words
+    int wl[2] = {0, 0}, wimax[2] = {0, 0}, n_wl = 0;
+    bool wl_more = false;                         // more than two loops: slow path
+    if (u_w < a.M) {
+        const int kw0 = u_w / G - k_lo;
+        const int kw1 = (min(a.M, u_w + 16 * RTW) - 1) / G - k_lo;
+        const int r_first = (row_at(kw0) >> 8) & 255, r_last = (row_at(kw1) >> 8) & 255;
+        // the last row of loop r_first inside [kw0, kw1]
+        const bool in0 = lane >= kw0 && lane <= kw1 && (int)((w0 >> 8) & 255) == r_first;
+        const bool in1 = lane + 64 >= kw0 && lane + 64 <= kw1 && (int)((w1 >> 8) & 255) == r_first;
+        const uint64_t b0 = __ballot(in0), b1 = __ballot(in1);
+        const int ka = b1 ? 64 + 63 - __builtin_clzll(b1) : 63 - __builtin_clzll(b0);
+        wl[0] = r_first;
+        wimax[0] = row_at(ka) & 255;
+        n_wl = 1;
+        if (r_last != r_first) {
+            wl[1] = (row_at(ka + 1) >> 8) & 255;
+            wimax[1] = row_at(kw1) & 255;
+            n_wl = 2;
+            wl_more = r_last != wl[1];
+        }
+    }
+    // prefetch the draft-block rows of up to two loops (keys < 8) into registers;
+    // piece pc = ((slot*2 + kv)*8 + key)*(D/8) + chunk, lane holds pc = lane + 64k
+    const bool pf_ok = kh == 0 && it.last && !wl_more && (n_wl < 1 || wimax[0] < 8) &&
+                       (n_wl < 2 || wimax[1] < 8);
+    uint4 pf[PF];
+    {
+        // wave-uniform bases of the (loop slot, K/V) block rows; lanes pick theirs
+        const uint16_t* pb[2][2];
+        int64_t pst[2];
 #pragma unroll
-            for (int tr = 0; tr < RTW; ++tr) {
-                if (base >= any_lim[tr]) continue;
-                if (!have) lds_frags<D>(stage, f, n, q);
-                have = true;
-                bool v[8];
-                const bool full = base + 32 <= full_lim[tr];
-                if (!full) {
+        for (int kv = 0; kv < 2; ++kv) {
+            const View& vw = kv ? a.bv : a.bk;
+            pst[kv] = vw.st;
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+                pb[sl][kv] = vw.p + it.b * vw.sb + (int64_t)((sl ? wl[1] : wl[0]) - 1) * vw.sp + it.g * vw.sh;
+        }
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const int pc = lane + 64 * k;
+            const int c8 = pc % (D / 8), rest = pc / (D / 8);
+            const int key = rest % 8, kv = (rest / 8) % 2, sl = rest / 16;
+            pf[k] = make_uint4(0, 0, 0, 0);
+            if (pf_ok && sl < n_wl && key < a.n_blk && key <= wimax[sl & 1]) {
+                const uint16_t* base = (sl & 1) ? (kv ? pb[1][1] : pb[1][0]) : (kv ? pb[0][1] : pb[0][0]);
+                pf[k] = *reinterpret_cast<const uint4*>(base + key * (kv ? pst[1] : pst[0]) + c8 * 8);
+            }
+        }
+    }
+
+
+    // Iteration j computes this half's tile j from registers; the key half of
+    // tile j + 1 is read from LDS once the scores of tile j are formed, its
+    // value half once O has taken tile j.  Tile j - 1 + S goes into the stage
+    // of tile j - 1, whose reads every wave finished before this barrier.
+    const int n_mine = kh == 0 ? n_iter : n_tiles / 2;   // tiles of this half
+    Frags<D> f;
+    // after this barrier the queries and every wave's part of tile 0 are in LDS
+    if (n_iter > 0) {
+        wait_tile(0);
+    } else {
+        __builtin_amdgcn_s_waitcnt(0xF70);
+        asm volatile("s_barrier" ::: "memory");
+    }
+#pragma unroll
+    for (int t = 0; t < RTW; ++t)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) rt[t].q[c] = s_q[rw][t * (D / 32) + c][lane];
+    if (n_mine > 0) {
+        lds_keys<D>(s_tile[0][kh], f, lane);
+        lds_values<D>(s_tile[0][kh], f, lane);
+    }
+    int sj = 0;                                   // stage of tile j
+    int sn = 1;                                   // stage of tile j + 1
+    auto advance = [&](int j) {
+        if (j + 1 < n_iter) wait_tile(j + 1);
+        const int sp = sj == 0 ? S - 1 : sj - 1;  // stage of tile j - 1
+        if (ti < n_tiles) issue_next(s_tile[sp][kh]);
+    };
+    auto next_keys = [&](int j) {
+        if (j + 1 < n_mine) lds_keys<D>(s_tile[sn][kh], f, lane);
+    };
+    auto next_values = [&](int j) {
+        if (j + 1 < n_mine) lds_values<D>(s_tile[sn][kh], f, lane);
+        sj = sn;
+        sn = sn == S - 1 ? 0 : sn + 1;
+    };
+    // fast phase: every row-head reads both tiles of the iteration in full
+    int j = 0;
+    for (; j < n_fast; ++j) {
+        advance(j);
+        float x[RTW][8];
+#pragma unroll
+        for (int tr = 0; tr < RTW; ++tr) tile_scores<D>(rt[tr], f, x[tr]);
+        next_keys(j);
+#pragma unroll
+        for (int tr = 0; tr < RTW; ++tr) tile_finish_full<D>(rt[tr], f, x[tr], sl2);
+        next_values(j);
+    }
+    // general phase: deep tiles with masks, then ring tiles
+    int cpl = 0, cst = 0;                         // ring cursor of the compute side
+    for (; j < n_iter; ++j) {
+        advance(j);
+        const int t = 2 * j + kh;
+        float x[RTW][8];
+        int mode[RTW];                            // 0 skip, 1 masked, 2 full
+        bool v[RTW][8];
+        if (t < n_tiles) {
+            if (t < n_deep) {
+                const int base = d0 + 32 * t;
+#pragma unroll
+                for (int tr = 0; tr < RTW; ++tr) {
+                    mode[tr] = base >= any_lim[tr] ? 0 : (base + 32 <= full_lim[tr] ? 2 : 1);
                     const int lim = min(rt[tr].e, d1);
                     const bool ok = RI_OK(rt[tr].ri);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = ok && base + key_of(e, q) < lim;
+                    for (int e = 0; e < 8; ++e) v[tr][e] = ok && base + key_of(e, q) < lim;
                 }
-                tile_update<D>(rt[tr], f, full, v, sl2);
+            } else {
+                if (t - 2 < n_deep) { cpl = 0; cst = t - n_deep; }
+                while (cst >= ring_tiles) { cst -= ring_tiles; ++cpl; }
+                const int r = cpl < 64 ? __builtin_amdgcn_readlane(loops_v0, cpl)
+                                       : __builtin_amdgcn_readlane(loops_v1, cpl - 64);
+                const int base = cst * 32;
+                cst += 2;
+#pragma unroll
+                for (int tr = 0; tr < RTW; ++tr) mode[tr] = mask_ring<D>(rt[tr], it, (int)a.WR, r, base, q, v[tr]);
             }
         } else {
-            int r, st;
-            ring_pos(t, r, st);
-            const int base = st * 32;
 #pragma unroll
-            for (int tr = 0; tr < RTW; ++tr) {
-                bool v[8];
-                if (mask_ring<D>(rt[tr], it, (int)a.WR, r, base, q, v)) {
-                    if (!have) lds_frags<D>(stage, f, n, q);
-                    have = true;
-                    tile_update<D>(rt[tr], f, false, v, sl2);
-                }
-            }
+            for (int tr = 0; tr < RTW; ++tr) mode[tr] = 0;
         }
+#pragma unroll
+        for (int tr = 0; tr < RTW; ++tr)
+            if (mode[tr]) tile_scores<D>(rt[tr], f, x[tr]);
+        next_keys(j);
+#pragma unroll
+        for (int tr = 0; tr < RTW; ++tr) {
+            if (mode[tr] == 2) tile_finish_full<D>(rt[tr], f, x[tr], sl2);
+            else if (mode[tr] == 1) tile_finish_masked<D>(rt[tr], f, x[tr], v[tr], sl2);
+        }
+        next_values(j);
     }
+    __builtin_amdgcn_s_waitcnt(0xF70);            // no direct load left in flight
 
-    // merge half 1 into half 0 (lane-wise: both hold the same row-heads); all
-    // stage loads completed in the last iterations
+    // merge half 1 into half 0 (lane-wise: both hold the same row-heads); the
+    // compiler waits here for every direct load still in flight
     lds_barrier();
     float* s_m = reinterpret_cast<float*>(&s_tile[0][0][0]);
     if (kh == 1) {
@@ -754,7 +1023,7 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
 #pragma unroll
     for (int tr = 0; tr < RTW; ++tr) {
         sum_lane_groups<D>(rt[tr]);
-        write_result<D>(a, s_rows, it, rt[tr], u_w + 16 * tr + n, q);
+        write_result_word<D>(a, it, rt[tr], u_w + 16 * tr + n, rword[tr], q);
     }
 }
 
@@ -1021,7 +1290,6 @@ hipError_t launch_verify_rows(const VerifyArgs& a, int rtw, hipStream_t s) {
         case 64 * 4 + 1: return launch_items(k_verify_rows<64, 1>, a, s, 512);
         case 64 * 4 + 2: return launch_items(k_verify_rows<64, 2>, a, s, 512);
         case 96 * 4 + 1: return launch_items(k_verify_rows<96, 1>, a, s, 512);
-        case 96 * 4 + 2: return launch_items(k_verify_rows<96, 2>, a, s, 512);
         case 128 * 4 + 1: return launch_items(k_verify_rows<128, 1>, a, s, 512);
     }
     return hipErrorInvalidValue;
