@@ -533,6 +533,10 @@ __device__ inline int wave_max(int x) { return wave_reduce<true>(x); }
 __device__ inline void dma16(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(lds) : "memory");
 }
+// 4 bytes per lane (lane l lands at lds + 4 l); same contract as dma16
+__device__ inline void dma4(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" :: "v"(g), "s"(lds) : "memory");
+}
 __device__ inline uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -729,26 +733,29 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
         iV += 2 * TILE;
         ++issued;
     };
-    // wait until tile j of this half is in LDS: this wave's loads of it are
-    // done when at most the tiles it issued later are outstanding (s_waitcnt
-    // vmcnt(N); 0xF70 leaves expcnt and lgkmcnt unconstrained); after the
-    // barrier every wave's part is there
-    auto wait_tile = [&](int j) {
-        const int later = issued - j - 1;
-        if (later >= 5) __builtin_amdgcn_s_waitcnt(0xF70 | (5 * PT));
-        else if (later == 4) __builtin_amdgcn_s_waitcnt(0xF70 | (4 * PT));
-        else if (later == 3) __builtin_amdgcn_s_waitcnt(0xF70 | (3 * PT));
-        else if (later == 2) __builtin_amdgcn_s_waitcnt(0xF70 | (2 * PT));
-        else if (later == 1) __builtin_amdgcn_s_waitcnt(0xF70 | PT);
-        else __builtin_amdgcn_s_waitcnt(0xF70);
-        asm volatile("s_barrier" ::: "memory");
+    // Past the end of its tiles a wave still issues one group of PT loads per
+    // step: PT 4-byte loads of valid memory into the stage the missing tile
+    // would use, which no later tile of this half uses.  Each step thus
+    // issues PT loads, and every wait is a constant count: tile j is in LDS
+    // when at most the groups issued after it are outstanding (s_waitcnt
+    // vmcnt(N); 0xF70 leaves expcnt and lgkmcnt unconstrained).  Constant
+    // waits keep the loop free of branches the compiler would thread across
+    // its back edge.
+    auto issue_dummy = [&](uint16_t* stage) {
+        const uint32_t l = lds_addr(stage);
+#pragma unroll
+        for (int k = 0; k < PT; ++k) dma4(gK + 2 * lane, l + 256 * k);
+        ti += 2;
+        ++issued;
     };
-    static_assert(5 * 4 <= 63, "vmcnt field");
+    static_assert((S - 2) * PT <= 63, "vmcnt field");
 
     // the first S - 1 tile pairs of this half (after the query loads, so the
     // wait for tile 0 covers them)
-    for (int j = 0; j < S - 1; ++j)
+    for (int j = 0; j < S - 1; ++j) {
         if (ti < n_tiles) issue_next(s_tile[j][kh]);
+        else issue_dummy(s_tile[j][kh]);
+    }
 
     // this wave's loops (ascending, at most two on the fast path) with their
     // largest block offsets, from the sorted row words
@@ -810,13 +817,11 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     // of tile j - 1, whose reads every wave finished before this barrier.
     const int n_mine = kh == 0 ? n_iter : n_tiles / 2;   // tiles of this half
     Frags<D> f;
-    // after this barrier the queries and every wave's part of tile 0 are in LDS
-    if (n_iter > 0) {
-        wait_tile(0);
-    } else {
-        __builtin_amdgcn_s_waitcnt(0xF70);
-        asm volatile("s_barrier" ::: "memory");
-    }
+    // after this barrier the queries and every wave's part of tile 0 are in
+    // LDS (the S - 2 groups issued after tile 0 may be outstanding); the asm
+    // text differs from the loop's barrier so the two are never merged
+    __builtin_amdgcn_s_waitcnt(0xF70 | ((S - 2) * PT));
+    asm volatile("s_barrier ; queries and tile 0" ::: "memory");
 #pragma unroll
     for (int t = 0; t < RTW; ++t)
 #pragma unroll
@@ -827,10 +832,13 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     }
     int sj = 0;                                   // stage of tile j
     int sn = 1;                                   // stage of tile j + 1
-    auto advance = [&](int j) {
-        if (j + 1 < n_iter) wait_tile(j + 1);
-        const int sp = sj == 0 ? S - 1 : sj - 1;  // stage of tile j - 1
-        if (ti < n_tiles) issue_next(s_tile[sp][kh]);
+    auto advance = [&](int) {
+        // tile j + 1 in LDS for every wave; every wave's reads of tile j - 1 done
+        __builtin_amdgcn_s_waitcnt(0xF70 | ((S - 3) * PT));
+        asm volatile("s_barrier" ::: "memory");
+        uint16_t* sp = s_tile[sj == 0 ? S - 1 : sj - 1][kh];   // stage of tile j - 1
+        if (ti < n_tiles) issue_next(sp);
+        else issue_dummy(sp);
     };
     auto next_keys = [&](int j) {
         if (j + 1 < n_mine) lds_keys<D>(s_tile[sn][kh], f, lane);
