@@ -104,8 +104,8 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here) {
     const int force_min_chunk = env_int("RIPE_MIN_CHUNK", 0);
     Plan p;
     p.M = rows_here * (g.Hq / g.Hkv);
-    // the rows kernel pays off once a KV head carries several hundred row-heads
-    p.rows_kernel = force_kernel ? force_kernel == 2 : p.M >= 512;
+    // the rows kernel pays off once a KV head carries a hundred row-heads or more
+    p.rows_kernel = force_kernel ? force_kernel == 2 : p.M >= 128;
     const int64_t heads = (int64_t)g.B * g.Hkv;
     int rows_per_item;
     if (p.rows_kernel) {

@@ -596,7 +596,7 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_tile[S][2][2 * TILE];
     __shared__ __attribute__((aligned(16))) uint4 s_q[4][RTW * (D / 32)][64];   // query operands per row group
     static_assert(4 * RTW * 64 * MS * 4 <= (int)sizeof(s_tile), "merge buffer");
-    static_assert(4 * 2 * TILE * 2 <= (int)sizeof(s_tile), "per-wave block scratch");
+    static_assert(8 * 2 * TILE * 2 <= (int)sizeof(s_tile), "per-wave block scratch");
     static_assert(RTW <= 2, "two row words per lane");
 
     const int tid = threadIdx.x;
@@ -780,33 +780,26 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
             wl_more = r_last != wl[1];
         }
     }
-    // prefetch the draft-block rows of up to two loops (keys < 8) into registers;
-    // piece pc = ((slot*2 + kv)*8 + key)*(D/8) + chunk, lane holds pc = lane + 64k
-    const bool pf_ok = kh == 0 && it.last && !wl_more && (n_wl < 1 || wimax[0] < 8) &&
-                       (n_wl < 2 || wimax[1] < 8);
-    uint4 pf[PF];
+    // Draft-block tiles: the wave's loop slot kh (its first or second loop)
+    // is applied by this wave before the halves merge.  Its rows (keys < 8)
+    // are prefetched into registers: piece pc = (kv*8 + key)*(D/8) + chunk,
+    // lane holds pc = lane + 64k.
+    constexpr int PB = D / 32;                   // prefetched pieces per lane
+    const bool pf_ok = it.last && !wl_more && kh < n_wl && (kh ? wimax[1] : wimax[0]) < 8;
+    uint4 pf[PB];
     {
-        // wave-uniform bases of the (loop slot, K/V) block rows; lanes pick theirs
-        const uint16_t* pb[2][2];
-        int64_t pst[2];
+        const int my_r = kh ? wl[1] : wl[0];
+        const int my_imax = kh ? wimax[1] : wimax[0];
+        const uint16_t* pbk = a.bk.p + it.b * a.bk.sb + (int64_t)(my_r - 1) * a.bk.sp + it.g * a.bk.sh;
+        const uint16_t* pbv = a.bv.p + it.b * a.bv.sb + (int64_t)(my_r - 1) * a.bv.sp + it.g * a.bv.sh;
 #pragma unroll
-        for (int kv = 0; kv < 2; ++kv) {
-            const View& vw = kv ? a.bv : a.bk;
-            pst[kv] = vw.st;
-#pragma unroll
-            for (int sl = 0; sl < 2; ++sl)
-                pb[sl][kv] = vw.p + it.b * vw.sb + (int64_t)((sl ? wl[1] : wl[0]) - 1) * vw.sp + it.g * vw.sh;
-        }
-#pragma unroll
-        for (int k = 0; k < PF; ++k) {
+        for (int k = 0; k < PB; ++k) {
             const int pc = lane + 64 * k;
             const int c8 = pc % (D / 8), rest = pc / (D / 8);
-            const int key = rest % 8, kv = (rest / 8) % 2, sl = rest / 16;
+            const int key = rest % 8, kv = rest / 8;
             pf[k] = make_uint4(0, 0, 0, 0);
-            if (pf_ok && sl < n_wl && key < a.n_blk && key <= wimax[sl & 1]) {
-                const uint16_t* base = (sl & 1) ? (kv ? pb[1][1] : pb[1][0]) : (kv ? pb[0][1] : pb[0][0]);
-                pf[k] = *reinterpret_cast<const uint4*>(base + key * (kv ? pst[1] : pst[0]) + c8 * 8);
-            }
+            if (pf_ok && key < a.n_blk && key <= my_imax)
+                pf[k] = *reinterpret_cast<const uint4*>((kv ? pbv + key * a.bv.st : pbk + key * a.bk.st) + c8 * 8);
         }
     }
 
@@ -906,8 +899,55 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0xF70);            // no direct load left in flight
 
-    // merge half 1 into half 0 (lane-wise: both hold the same row-heads); the
-    // compiler waits here for every direct load still in flight
+    // every wave's loads are done and every wave has left the stages
+    lds_barrier();
+    // draft-block tiles of the wave's loop slot kh, staged in a wave-private
+    // part of the stages (K in storage order, V transposed)
+    if (it.last && kh < n_wl) {
+        uint16_t* sk = &s_tile[0][0][0] + (rw * 2 + kh) * 2 * TILE;
+        uint16_t* sv = sk + TILE;
+        const int r = kh ? wl[1] : wl[0];
+        const int imax = kh ? wimax[1] : wimax[0];
+        const uint16_t* bK = a.bk.p + it.b * a.bk.sb + (int64_t)(r - 1) * a.bk.sp + it.g * a.bk.sh;
+        const uint16_t* bV = a.bv.p + it.b * a.bv.sb + (int64_t)(r - 1) * a.bv.sp + it.g * a.bv.sh;
+        for (int base = 0; base <= imax; base += 32) {
+            if (pf_ok) {
+                for (int z = lane; z < 2 * TILE / 8; z += 64)
+                    *reinterpret_cast<uint4*>(sk + z * 8) = make_uint4(0, 0, 0, 0);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int k = 0; k < PB; ++k) {
+                    const int pc = lane + 64 * k;
+                    const int c8 = pc % (D / 8), rest = pc / (D / 8);
+                    const int key = rest % 8, kv = rest / 8;
+                    if (kv == 0) {
+                        *reinterpret_cast<uint4*>(sk + key_off(key, c8 * 8, D)) = pf[k];
+                    } else {
+                        const uint32_t w[4] = {pf[k].x, pf[k].y, pf[k].z, pf[k].w};
+#pragma unroll
+                        for (int cc = 0; cc < 8; ++cc)
+                            sv[val_off(key, c8 * 8 + cc, D)] = (uint16_t)(w[cc >> 1] >> (16 * (cc & 1)));
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            } else {
+                stage_block<D>(a, bK, bV, base, sk, sv, lane);
+            }
+            Frags<D> f;
+            load_frags<D>(sk, sv, f, n, q);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int tr = 0; tr < RTW; ++tr) {
+                bool v[8];
+                if (mask_block<D>(rt[tr], r, base, q, v)) tile_update<D>(rt[tr], f, false, v, sl2);
+            }
+        }
+    }
+
+    // merge half 1 into half 0 (lane-wise: both hold the same row-heads)
     lds_barrier();
     float* s_m = reinterpret_cast<float*>(&s_tile[0][0][0]);
     if (kh == 1) {
@@ -945,50 +985,6 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     if (it.last) {
         uint16_t* sk = &s_tile[0][0][0] + rw * 2 * TILE;   // per-wave scratch in the stages
         uint16_t* sv = sk + TILE;
-        // draft-block keys of the wave's loops: from the prefetched registers when
-        // they fit, else staged straight from the caller's buffer
-        for (int sl = 0; sl < n_wl; ++sl) {
-            const int r = sl ? wl[1] : wl[0];
-            const int imax = sl ? wimax[1] : wimax[0];
-            const uint16_t* bK = a.bk.p + it.b * a.bk.sb + (int64_t)(r - 1) * a.bk.sp + it.g * a.bk.sh;
-            const uint16_t* bV = a.bv.p + it.b * a.bv.sb + (int64_t)(r - 1) * a.bv.sp + it.g * a.bv.sh;
-            for (int base = 0; base <= imax; base += 32) {
-                if (pf_ok) {
-                    for (int z = lane; z < 2 * TILE / 8; z += 64)
-                        *reinterpret_cast<uint4*>(sk + z * 8) = make_uint4(0, 0, 0, 0);
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                    for (int k = 0; k < PF; ++k) {
-                        const int pc = lane + 64 * k;
-                        const int c8 = pc % (D / 8), rest = pc / (D / 8);
-                        const int key = rest % 8, kv = (rest / 8) % 2, psl = rest / 16;
-                        if (psl != sl) continue;
-                        if (kv == 0) {
-                            *reinterpret_cast<uint4*>(sk + key_off(key, c8 * 8, D)) = pf[k];
-                        } else {
-                            const uint32_t w[4] = {pf[k].x, pf[k].y, pf[k].z, pf[k].w};
-#pragma unroll
-                            for (int cc = 0; cc < 8; ++cc)
-                                sv[val_off(key, c8 * 8 + cc, D)] = (uint16_t)(w[cc >> 1] >> (16 * (cc & 1)));
-                        }
-                    }
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                    __builtin_amdgcn_wave_barrier();
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                } else {
-                    stage_block<D>(a, bK, bV, base, sk, sv, lane);
-                }
-                Frags<D> f;
-                load_frags<D>(sk, sv, f, n, q);
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int tr = 0; tr < RTW; ++tr) {
-                    bool v[8];
-                    if (mask_block<D>(rt[tr], r, base, q, v)) tile_update<D>(rt[tr], f, false, v, sl2);
-                }
-            }
-        }
         if (wl_more) {
             // loops beyond the first two (unusual row sets): smallest remaining first
             int done = 0;
