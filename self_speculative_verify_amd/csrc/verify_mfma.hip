@@ -785,9 +785,11 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     // are prefetched into registers: piece pc = (kv*8 + key)*(D/8) + chunk,
     // lane holds pc = lane + 64k.
     constexpr int PB = D / 32;                   // prefetched pieces per lane
-    const bool pf_ok = it.last && !wl_more && kh < n_wl && (kh ? wimax[1] : wimax[0]) < 8;
+    // (not with 256 dims of row tiles per wave, whose steps need those registers)
+    constexpr bool kPf = D * RTW < 256;
+    const bool pf_ok = kPf && it.last && !wl_more && kh < n_wl && (kh ? wimax[1] : wimax[0]) < 8;
     uint4 pf[PB];
-    {
+    if (kPf) {
         const int my_r = kh ? wl[1] : wl[0];
         const int my_imax = kh ? wimax[1] : wimax[0];
         const uint16_t* pbk = a.bk.p + it.b * a.bk.sb + (int64_t)(my_r - 1) * a.bk.sp + it.g * a.bk.sh;
@@ -1274,7 +1276,7 @@ hipError_t launch_items(K kern, const VerifyArgs& a, hipStream_t s, int threads 
 }  // namespace
 
 int keys_max_row_tiles(int d) { return d == 128 ? 1 : 2; }
-int rows_max_row_tiles(int d) { return d == 64 ? 2 : 1; }
+int rows_max_row_tiles(int d) { return d == 96 ? 1 : 2; }
 
 hipError_t launch_verify_keys(const VerifyArgs& a, int rt, hipStream_t s) {
     if (rt < 1 || rt > keys_max_row_tiles(a.d)) return hipErrorInvalidValue;
@@ -1295,6 +1297,7 @@ hipError_t launch_verify_rows(const VerifyArgs& a, int rtw, hipStream_t s) {
         case 64 * 4 + 2: return launch_items(k_verify_rows<64, 2>, a, s, 512);
         case 96 * 4 + 1: return launch_items(k_verify_rows<96, 1>, a, s, 512);
         case 128 * 4 + 1: return launch_items(k_verify_rows<128, 1>, a, s, 512);
+        case 128 * 4 + 2: return launch_items(k_verify_rows<128, 2>, a, s, 512);
     }
     return hipErrorInvalidValue;
 }

@@ -35,12 +35,16 @@ def _gpu():
 
 # Every case runs through both matrix-core kernels: the planner's choice, and
 # the other one forced (RIPE_KERNEL=1: waves split keys; 2: waves own rows),
-# each with one chunk and with several chunks per sequence (combine kernel).
-@pytest.fixture(params=["auto", "keys", "rows", "keys-chunked", "rows-chunked"], autouse=True)
+# each with one chunk and with several chunks per sequence (combine kernel),
+# and the rows kernel with two row tiles per wave where the head size allows.
+@pytest.fixture(params=["auto", "keys", "rows", "rows-2tiles", "keys-chunked", "rows-chunked"], autouse=True)
 def kernel_choice(request, monkeypatch):
-    kern = {"auto": None, "keys": "1", "rows": "2", "keys-chunked": "1", "rows-chunked": "2"}[request.param]
+    kern = {"auto": None, "keys": "1", "rows": "2", "rows-2tiles": "2", "keys-chunked": "1",
+            "rows-chunked": "2"}[request.param]
     if kern:
         monkeypatch.setenv("RIPE_KERNEL", kern)
+    if request.param == "rows-2tiles":
+        monkeypatch.setenv("RIPE_ROW_TILES", "2")
     if request.param.endswith("chunked"):
         monkeypatch.setenv("RIPE_ITEMS_TARGET", "100000")
         monkeypatch.setenv("RIPE_MIN_CHUNK", "32")
