@@ -843,8 +843,17 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
         sj = sn;
         sn = sn == S - 1 ? 0 : sn + 1;
     };
-    // fast phase: every row-head reads both tiles of the iteration in full
+    // A wave without valid row-heads (the workgroup's last row block, or few
+    // rows) only takes its part in the loads and barriers.
     int j = 0;
+    if (u_w >= a.M) {
+        for (; j < n_iter; ++j) {
+            advance(j);
+            sj = sn;                              // the stage cursors still move
+            sn = sn == S - 1 ? 0 : sn + 1;
+        }
+    }
+    // fast phase: every row-head reads both tiles of the iteration in full
     for (; j < n_fast; ++j) {
         advance(j);
         float x[RTW][8];
