@@ -12,6 +12,12 @@ Prints one JSON line: unique-KV GB/s (value), verified tokens/s, the roofline
 of the verify launch (HBM bytes or matrix-core flops, whichever bounds the
 workload), and the fp64 oracle timed on the host cores on a bounded sample
 (whole layers) of the same workload.
+
+``--mode per-loop`` times the same step as a forward pass runs it, R calls of
+the D rows of one loop per layer; ``--mode draft`` times the draft pass,
+D x r_draft calls of one row each (block keys 0..j).  Their value is the sum
+of every call's unique-KV bytes over the step time; ``bytes_vs_batched`` says
+how many more bytes that is than the batched call.
 """
 from __future__ import annotations
 
@@ -48,6 +54,11 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graphs")
+    ap.add_argument("--mode", default="batched", choices=["batched", "per-loop", "draft"],
+                    help="call schedule: the D x R grid in one call per layer (batched), "
+                         "R calls of D rows (per-loop), or the draft pass of D x r_draft "
+                         "single-row calls (draft)")
+    ap.add_argument("--draft-loops", type=int, default=4, help="r_draft of the draft pass")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -139,19 +150,23 @@ def time_append(wl, window, anchor, dev, n_rep):
             "GB/s": round(2 * moved / (us * 1e-6) / 1e9, 2), "tokens_per_seq": D}
 
 
-def cpu_baseline(wl, window, anchor, rows):
-    """The fp64 oracle on whole layers of the workload (same rows, every head),
-    layer after layer until CPU_SAMPLE_S seconds are spent."""
+def cpu_baseline(wl, window, anchor, calls):
+    """The fp64 oracle on whole layers of the workload (the same calls, every
+    head), layer after layer until CPU_SAMPLE_S seconds are spent."""
+    import numpy as np
     import oracle
     spent, u, n_layers = 0.0, 0, 0
+    rows = [x for c in calls for x in c.rows]
     for layer in range(wl.n_layers):
         oc = oracle.prefix_cache(wl, layers=[layer], anchor=anchor, window=window)
         q = wl.queries(layer)
         bk, bv = wl.block(layer)
-        t0 = time.perf_counter()
-        oc.verify(layer, rows, q, bk, bv, wl.n_blk)
-        spent += time.perf_counter() - t0
-        u += unique_kv_bytes(wl, window, anchor, rows, wl.lens)
+        for c in calls:
+            qc = np.ascontiguousarray(q[:, [wl.rows.index(x) for x in c.rows]])
+            t0 = time.perf_counter()
+            oc.verify(layer, c.rows, qc, bk, bv, c.n_blk)
+            spent += time.perf_counter() - t0
+            u += unique_kv_bytes(wl, window, anchor, c.rows, wl.lens)
         n_layers += 1
         del oc
         if spent >= CPU_SAMPLE_S:
@@ -159,7 +174,7 @@ def cpu_baseline(wl, window, anchor, rows):
     rounds = n_layers / wl.n_layers
     return {"value": round(u / spent / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"{n_layers} of {wl.n_layers} layers: all {len(rows)} rows x {wl.n_heads_q} "
+            "sample": f"{n_layers} of {wl.n_layers} layers: {len(calls)} call(s), {len(rows)} rows x {wl.n_heads_q} "
                       f"heads x {wl.batch} sequences, {spent:.1f} s",
             "tokens_per_s": round(wl.batch * len({i for i, _ in rows}) * rounds / spent, 3)}
 
@@ -175,15 +190,30 @@ def main():
     import ripe_harness as H
     from synth import WINDOW_FULL, named_workload
 
+    from self_speculative_verify_amd import schedule
+
     wl = named_workload(args.workload)
     window = WINDOW_FULL if args.full else (wl.window if args.window is None else args.window)
     anchor = wl.anchor if args.anchor is None else args.anchor
     rows = wl.rows
+    if args.mode == "batched":
+        calls = [schedule.Call(list(rows), wl.n_blk)]
+    elif rows != schedule.batched_verify(wl.n_blk, wl.n_loops)[0].rows:
+        print(f"--mode {args.mode} needs a workload that verifies the whole D x R grid",
+              file=sys.stderr)
+        sys.exit(2)
+    elif args.mode == "per-loop":
+        calls = schedule.per_loop_verify(wl.n_blk, wl.n_loops)
+    else:
+        calls = schedule.draft_pass(wl.n_blk, min(args.draft_loops, wl.n_loops))
+    call_idx = [[rows.index(x) for x in c.rows] for c in calls]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    u_layer = unique_kv_bytes(wl, window, anchor, rows, wl.lens)
-    f_layer = flops(wl, rows, wl.lens)
+    # algorithmic bytes and flops of one layer (all its calls)
+    u_calls = [unique_kv_bytes(wl, window, anchor, c.rows, wl.lens) for c in calls]
+    f_calls = [flops(wl, c.rows, wl.lens) for c in calls]
+    u_layer, f_layer = sum(u_calls), sum(f_calls)
     u_round = u_layer * wl.n_layers
     copies = args.copies or max(2, 1 + math.ceil(2 * MALL_BYTES / max(u_round, 1)))
     print(f"bench: {wl.name} W={window} anchor={anchor} copies={copies}", file=sys.stderr, flush=True)
@@ -202,23 +232,32 @@ def main():
     for c in range(copies):
         cache = H.make_cache(wl, device=dev, window=window, anchor=anchor)
         H.load_prefix(cache, wl, device=dev)
-        ins = [H.verify_inputs(wl, layer, device=dev) for layer in range(wl.n_layers)]
-        outs = [(torch.empty((wl.batch, len(rows), wl.n_heads_q, wl.head_dim), device=dev),
-                 torch.empty((wl.batch, len(rows), wl.n_heads_q), device=dev))
+        ins = []
+        for layer in range(wl.n_layers):
+            q, bk, bv = H.verify_inputs(wl, layer, device=dev)
+            qs = [q if len(calls) == 1 else q[:, idx].contiguous() for idx in call_idx]
+            ins.append((qs, bk, bv))
+        outs = [[(torch.empty((wl.batch, len(c.rows), wl.n_heads_q, wl.head_dim), device=dev),
+                  torch.empty((wl.batch, len(c.rows), wl.n_heads_q), device=dev)) for c in calls]
                 for _ in range(wl.n_layers)]
         setups.append((cache, ins, outs))
     memo.clear()
     wl.prefix = orig_prefix
     torch.cuda.synchronize()
 
-    def run_layer(setup, layer):
+    def run_call(setup, k, layer):
         cache, ins, outs = setup
-        q, bk, bv = ins[layer]
-        cache.verify(layer, rows, q, bk, bv, wl.n_blk, out=outs[layer][0], lse=outs[layer][1])
+        qs, bk, bv = ins[layer]
+        c = calls[k]
+        cache.verify(layer, c.rows, qs[k], bk, bv, c.n_blk, out=outs[layer][k][0],
+                     lse=outs[layer][k][1])
 
     def run_round(setup):
-        for layer in range(wl.n_layers):
-            run_layer(setup, layer)
+        # the order a forward pass runs: call by call (loop by loop), each
+        # through all layers
+        for k in range(len(calls)):
+            for layer in range(wl.n_layers):
+                run_call(setup, k, layer)
 
     for s in setups:            # eager warm-up (allocates workspaces outside capture)
         run_round(s)
@@ -250,21 +289,23 @@ def main():
     ms = start.elapsed_time(stop) / max(args.steps, 1)
     t = ms / 1e3
 
-    # per-launch duration of ripe_verify_attn: events between launches queued
+    # per-call duration of ripe_verify_attn: events between calls queued
     # behind a spinning kernel, so no host gap falls between them
-    n_rep = max(1, min(args.steps, 20))
+    n_rep = max(1, min(args.steps, 20 if len(calls) == 1 else 2))
     launch_ms = []
+    n_ev = len(calls) * wl.n_layers
     for k in range(n_rep):
         torch.cuda._sleep(SPIN_CYCLES)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(wl.n_layers + 1)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)]
         s = setups[k % copies]
         evs[0].record()
-        for layer in range(wl.n_layers):
-            run_layer(s, layer)
-            evs[layer + 1].record()
+        for j in range(n_ev):
+            run_call(s, j // wl.n_layers, j % wl.n_layers)
+            evs[j + 1].record()
         torch.cuda.synchronize()
-        launch_ms += [evs[j].elapsed_time(evs[j + 1]) for j in range(wl.n_layers)]
+        launch_ms += [evs[j].elapsed_time(evs[j + 1]) for j in range(n_ev)]
     launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    u_call, f_call = u_layer / len(calls), f_layer / len(calls)
     del setups, graphs
     append = time_append(wl, window, anchor, dev, n_rep)
 
@@ -277,27 +318,31 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    n_verified = wl.batch * len({i for i, _ in rows})   # draft positions verified per step
+    # block positions verified (or, for the draft pass, drafted) per step
+    n_tokens = wl.batch * len({i for i, _ in rows})
     gbs = u_round / t / 1e9
-    hbm_time = u_layer / (HBM_PEAK_GBS * 1e9)
-    mfma_time = f_layer / (MFMA_BF16_PEAK_TFS * 1e12)
+    hbm_time = u_call / (HBM_PEAK_GBS * 1e9)
+    mfma_time = f_call / (MFMA_BF16_PEAK_TFS * 1e12)
     digest = src_digest()
-    traffic = stored_traffic(args.workload, digest) if window == wl.window and anchor == wl.anchor else None
+    traffic_key = args.workload if args.mode == "batched" else f"{args.workload}:{args.mode}"
+    traffic = (stored_traffic(traffic_key, digest)
+               if window == wl.window and anchor == wl.anchor else None)
     if hbm_time >= mfma_time:
-        roof = {"bound": "hbm", "achieved": round(u_layer / launch_s / 1e9, 2), "peak": HBM_PEAK_GBS,
+        roof = {"bound": "hbm", "achieved": round(u_call / launch_s / 1e9, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": round(f_layer / launch_s / 1e12, 2),
+        roof = {"bound": "mfma", "achieved": round(f_call / launch_s / 1e12, 2),
                 "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = traffic
     roof["launch_us"] = round(launch_s * 1e6, 3)
-    roof["algorithmic_bytes"] = u_layer
-    roof["algorithmic_flops"] = f_layer
+    roof["algorithmic_bytes"] = round(u_call)
+    roof["algorithmic_flops"] = round(f_call)
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(wl, window, anchor, rows)
+        cpu = cpu_baseline(wl, window, anchor, calls)
+    u_batched = unique_kv_bytes(wl, window, anchor, rows, wl.lens)
 
     res = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
@@ -308,10 +353,14 @@ def main():
                    "heads_q": wl.n_heads_q, "heads_kv": wl.n_heads_kv, "head_dim": wl.head_dim,
                    "window": "full" if window == WINDOW_FULL else window, "block": wl.n_blk,
                    "batch": wl.batch, "lens": wl.lens if wl.batch <= 8 else "ragged",
-                   "rows_per_call": len(rows), "anchor": "query" if anchor == 0 else "cache",
+                   "mode": args.mode, "calls_per_layer": len(calls),
+                   **({"draft_loops": min(args.draft_loops, wl.n_loops)} if args.mode == "draft" else {}),
+                   "rows_per_call": len(rows) // len(calls),
+                   "anchor": "query" if anchor == 0 else "cache",
                    "cache_copies": copies, "timing": "eager" if args.eager else "hip-graph"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "tokens_per_s": round(n_verified / t, 1),
+        "tokens_per_s": round(n_tokens / t, 1),
+        "bytes_vs_batched": round(u_layer / u_batched, 4),
         "unique_kv_bytes_per_step": u_round,
         "flops_per_step": f_layer * wl.n_layers,
         "kernel_sources": digest,
