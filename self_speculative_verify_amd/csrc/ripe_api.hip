@@ -75,17 +75,20 @@ bool view_ok(const ripe_kv_view& v) {
 }
 
 // How one launch covers a call.  Row-heads (query row x query head of a KV
-// group) of a KV head: with 64 or more the "rows" kernel gives each wave 16*rt
-// of them and a workgroup 64*rt; with fewer the "keys" kernel gives a whole
-// workgroup 16*rt and splits the key tiles between its waves.  Committed
-// positions split into nc chunks of cl positions (a multiple of 32) when the
-// row blocks alone give too few workgroups for 256 compute units and the
-// chunks stay long enough that their partial states cost little next to the
-// keys they read.
+// group) of a KV head: with 128 or more the "rows" kernel gives each wave
+// 16*rt of them and a workgroup 64*rt; with fewer the "keys" kernel gives a
+// whole workgroup 16*rt and splits the key tiles between its waves.
+// Committed positions split into chunks of cl (a multiple of 32) when the row
+// blocks alone leave workgroup slots of the chip empty (one rows workgroup or
+// two keys workgroups fit on a compute unit); the count stops at one round of
+// slots, so no workgroup waits for another to finish, and at chunks long
+// enough that their partial states cost little next to the keys they read.
+// The last chunk of a sequence also takes the ring and draft-block tiles of
+// its row block, so it reads cx fewer committed positions than the others.
 struct Plan {
     bool rows_kernel;
     int rt, nrb, nc, n_groups, M;
-    int64_t cl;
+    int64_t cl, cx;
     size_t ws_bytes;
 };
 
@@ -95,10 +98,36 @@ int env_int(const char* name, int fallback) {
     return v > 0 ? v : fallback;
 }
 
-Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here) {
+// Tiles of the ring and draft-block work of the heaviest row block (rows:
+// sorted row words of the launch; null for a bound over every row set).
+int64_t extra_tiles(const Geometry& g, const uint32_t* rows, int rows_here, int M, int nrb,
+                    int rows_per_item, int64_t lmax) {
+    const int G = g.Hq / g.Hkv;
+    const int64_t ring_tiles = g.R > 1 ? (std::min<int64_t>(g.WR, lmax) + 31) / 32 : 0;
+    if (!rows) {
+        const int64_t nl = std::min<int64_t>(rows_per_item / G + 1, g.R);
+        return nl * ring_tiles + nl * ((g.max_block + 31) / 32);
+    }
+    int64_t most = 0;
+    for (int rb = 0; rb < nrb; ++rb) {
+        const int k_lo = rb * rows_per_item / G;
+        const int k_hi = std::min(rows_here, (std::min(M, (rb + 1) * rows_per_item) + G - 1) / G);
+        int64_t t = 0;
+        for (int k = k_lo; k < k_hi; ++k) {
+            const int r = (rows[k] >> 8) & 255, i = rows[k] & 255;
+            const bool first = k == k_lo || (int)((rows[k - 1] >> 8) & 255) != r;
+            const bool last = k + 1 == k_hi || (int)((rows[k + 1] >> 8) & 255) != r;
+            if (first && r < g.R) t += ring_tiles;
+            if (last) t += i / 32 + 1;     // rows of a loop are sorted by offset
+        }
+        most = std::max(most, t);
+    }
+    return most;
+}
+
+Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint32_t* rows) {
     // tuning and test overrides: workgroup target, row tiles, kernel (1 keys, 2 rows)
     const int target_env = env_int("RIPE_ITEMS_TARGET", 0);
-    const int target = target_env ? target_env : 512;
     const int force_rt = env_int("RIPE_ROW_TILES", 0);
     const int force_kernel = env_int("RIPE_KERNEL", 0);
     const int force_min_chunk = env_int("RIPE_MIN_CHUNK", 0);
@@ -122,18 +151,37 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here) {
     p.nrb = (p.M + rows_per_item - 1) / rows_per_item;
     int64_t lmax = 0;
     for (int b = 0; b < g.B; ++b) lmax = std::max<int64_t>(lmax, lens[b]);
-    const int64_t base = heads * p.nrb;
-    int64_t nc = 1;
-    // split the committed positions only when the row blocks alone leave a
-    // quarter of the compute units idle; then aim for `target` workgroups
-    if (base < target && (target_env || base < 192)) {
-        const int64_t min_chunk = force_min_chunk ? force_min_chunk : std::max<int64_t>(256, 8 * rows_per_item);
-        nc = std::max<int64_t>(1, std::min<int64_t>((target + base - 1) / base, lmax / min_chunk));
+    // workgroups of one (sequence, chunk) pair, and of the whole call unsplit
+    const int64_t units = (int64_t)g.Hkv * p.nrb;
+    const int64_t base = g.B * units;
+    const int64_t slots = target_env ? target_env : (p.rows_kernel ? 256 : 512);
+    const int64_t cx = 32 * extra_tiles(g, rows, rows_here, p.M, p.nrb, rows_per_item, lmax);
+    const int64_t min_chunk = force_min_chunk ? force_min_chunk : std::max<int64_t>(256, 8 * rows_per_item);
+    // One chunk length for every sequence, from their total: the pairs that
+    // fit one round of slots share the work evenly however ragged the
+    // lengths are (a sequence gets ceil((L + cx) / cl) chunks).
+    int64_t cl = 0, nc_cap = 1;
+    if (base < slots) {
+        int64_t sum = 0;
+        for (int b = 0; b < g.B; ++b) sum += lens[b] > 0 ? lens[b] + cx : 0;
+        const int64_t pairs = slots / units;
+        cl = std::max<int64_t>(min_chunk, up((sum + pairs - 1) / std::max<int64_t>(pairs, 1), 32));
+        // a bound on the chunk count that never falls as rows or lengths grow
+        nc_cap = std::max<int64_t>(1, std::min<int64_t>(pairs, (lmax + cx + min_chunk - 1) / min_chunk));
     }
-    p.cl = std::max<int64_t>(32, up((lmax + nc - 1) / nc, 32));
-    p.nc = (int)std::max<int64_t>(1, (lmax + p.cl - 1) / p.cl);
+    if (cl == 0 || cl >= lmax + cx) {
+        p.cx = 0;
+        p.cl = std::max<int64_t>(32, up(lmax, 32));
+        p.nc = 1;
+    } else {
+        p.cx = cx;
+        p.cl = cl;
+        p.nc = (int)((lmax + cx + cl - 1) / cl);
+    }
     p.n_groups = (int)(heads * p.nc);
-    p.ws_bytes = p.nc > 1 ? (size_t)heads * p.nc * p.M * (g.d + 2) * sizeof(float) : 0;
+    // whenever a split is possible, so a size queried for a row count holds
+    // for every row set of that size
+    p.ws_bytes = base < slots ? (size_t)heads * nc_cap * p.M * (g.d + 2) * sizeof(float) : 0;
     return p;
 }
 
@@ -272,7 +320,7 @@ size_t ripe_workspace_bytes(const ripe_cache* cache, int32_t n_rows) {
     size_t ws = 0;
     for (int layer = 0; layer < g.n_layers; ++layer) {   // any layer may be verified
         const int rows_here = std::min(ripe::kMaxRowsPerLaunch, (int)n_rows);
-        ws = std::max(ws, make_plan(g, lens + (size_t)layer * g.B, rows_here).ws_bytes);
+        ws = std::max(ws, make_plan(g, lens + (size_t)layer * g.B, rows_here, nullptr).ws_bytes);
     }
     return ws;
 }
@@ -327,8 +375,8 @@ ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
     for (int k0 = 0; k0 < n_rows; k0 += ripe::kMaxRowsPerLaunch) {
         a.rows_here = std::min(ripe::kMaxRowsPerLaunch, n_rows - k0);
         for (int k = 0; k < a.rows_here; ++k) a.rows[k] = rows[k0 + k];
-        const Plan p = make_plan(g, lens, a.rows_here);
-        a.M = p.M; a.nrb = p.nrb; a.nc = p.nc; a.cl = p.cl; a.n_groups = p.n_groups;
+        const Plan p = make_plan(g, lens, a.rows_here, a.rows);
+        a.M = p.M; a.nrb = p.nrb; a.nc = p.nc; a.cl = p.cl; a.cx = p.cx; a.n_groups = p.n_groups;
         const hipError_t e = p.rows_kernel ? ripe::launch_verify_rows(a, p.rt, stream)
                                            : ripe::launch_verify_keys(a, p.rt, stream);
         if (e != hipSuccess) return RIPE_EDEVICE;

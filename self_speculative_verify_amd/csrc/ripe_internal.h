@@ -87,6 +87,8 @@ struct VerifyArgs {
     int32_t nrb;             // row blocks per KV head
     int32_t nc;              // chunks of the longest sequence
     int64_t cl;              // positions per chunk
+    int64_t cx;              // positions' worth of ring and block tiles that the
+                             // last chunk of a sequence carries besides its own
     int32_t n_groups;        // B * Hkv * nc
     // rows of this launch sorted by (loop, block offset):
     // bits 0..7 block offset, 8..15 loop, 16..31 row index in the call

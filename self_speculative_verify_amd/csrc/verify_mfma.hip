@@ -334,7 +334,7 @@ __device__ inline bool decode_item(const VerifyArgs& a, Item& it) {
     it.g = bg % a.Hkv;
     it.b = bg / a.Hkv;
     it.L = a.lens[it.b];
-    it.nc_b = it.L > 0 ? (int)((it.L + a.cl - 1) / a.cl) : 1;
+    it.nc_b = it.L > 0 ? (int)((it.L + a.cx + a.cl - 1) / a.cl) : 1;
     if (it.c >= it.nc_b) return false;
     it.last = it.c == it.nc_b - 1;
     it.nsl = (int)min(a.WR, (int64_t)it.L);
@@ -348,11 +348,6 @@ __device__ inline int e_row(const VerifyArgs& a, int L, int i, int r) {
     if (r == a.R) return L;
     const int64_t beta = a.anchor == 0 ? (int64_t)L + i - a.W : (int64_t)L - a.W;
     return (int)(beta < 0 ? 0 : (beta > L ? L : beta));
-}
-
-// the launch's row table, copied from the kernel arguments into LDS once
-__device__ inline void stage_rows(const VerifyArgs& a, uint32_t* s_rows) {
-    for (int k = threadIdx.x; k < a.rows_here; k += blockDim.x) s_rows[k] = a.rows[k];
 }
 
 // state of row-head u (query row word `rw`, see VerifyArgs::rows); row-heads
@@ -373,11 +368,6 @@ __device__ inline void init_row_word(const VerifyArgs& a, const Item& it, int u,
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
         rt.q[c] = ok ? *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * q) : make_uint4(0, 0, 0, 0);
-}
-template <int D>
-__device__ inline void init_row(const VerifyArgs& a, const uint32_t* s_rows, const Item& it, int u,
-                                int q, RowTile<D>& rt) {
-    init_row_word<D>(a, it, u, s_rows[u < a.M ? u / a.group : 0], q, rt);
 }
 
 // masks of one row tile against a deep / ring / block tile; false = the tile
@@ -415,23 +405,43 @@ __device__ inline int mask_block(const RowTile<D>& rt, int r, int base, int q, b
 }
 
 // stage 32 draft-block keys/values (caller's [token][dim] layout) into a
-// wave-private LDS tile pair in the storage's operand order
+// wave-private LDS tile pair in the storage's operand order; keys past n_blk
+// are zero.  A lane holds D/16 16-byte pieces of K and of V; they are loaded
+// two at a time before any is stored (128 pieces of a wave cover at least
+// eight keys), and a group of pieces that lies wholly past n_blk is not
+// loaded at all, so a block of up to eight tokens costs one memory round trip.
 template <int D>
 __device__ inline void stage_block(const VerifyArgs& a, const uint16_t* K, const uint16_t* V,
                                    int base, uint16_t* sk, uint16_t* sv, int lane) {
-    for (int it = lane; it < 32 * (D / 8); it += 64) {
-        const int key = it / (D / 8), e0 = (it % (D / 8)) * 8;
-        const int jj = base + key;
-        uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-        if (jj < a.n_blk) {
-            kx = *reinterpret_cast<const uint4*>(K + jj * a.bk.st + e0);
-            vx = *reinterpret_cast<const uint4*>(V + jj * a.bv.st + e0);
-        }
-        *reinterpret_cast<uint4*>(sk + key_off(key, e0, D)) = kx;
-        const uint32_t w[4] = {vx.x, vx.y, vx.z, vx.w};
+    constexpr int PK = D / 8;                 // pieces per key row
+    constexpr int NI = 32 * PK / 64;          // pieces per lane
+    constexpr int GP = 2;                     // pieces loaded before any is stored
+    const int n_keys = a.n_blk - base;        // keys of this tile inside the block
+#pragma unroll 1
+    for (int t0 = 0; t0 < NI; t0 += GP) {
+        uint4 kx[GP], vx[GP];
+        const bool need = t0 * 64 < n_keys * PK;          // wave-uniform
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc)
-            sv[val_off(key, e0 + cc, D)] = (uint16_t)(w[cc >> 1] >> (16 * (cc & 1)));
+        for (int u = 0; u < GP; ++u) {
+            kx[u] = vx[u] = make_uint4(0, 0, 0, 0);
+            const int it = lane + 64 * (t0 + u);
+            const int key = it / PK, e0 = (it % PK) * 8;
+            if (need && t0 + u < NI && key < n_keys) {
+                kx[u] = *reinterpret_cast<const uint4*>(K + (base + key) * a.bk.st + e0);
+                vx[u] = *reinterpret_cast<const uint4*>(V + (base + key) * a.bv.st + e0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < GP; ++u) {
+            if (t0 + u >= NI) break;
+            const int it = lane + 64 * (t0 + u);
+            const int key = it / PK, e0 = (it % PK) * 8;
+            *reinterpret_cast<uint4*>(sk + key_off(key, e0, D)) = kx[u];
+            const uint32_t w[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc)
+                sv[val_off(key, e0 + cc, D)] = (uint16_t)(w[cc >> 1] >> (16 * (cc & 1)));
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -466,13 +476,6 @@ __device__ inline void write_result_word(const VerifyArgs& a, const Item& it, co
         if (q == 0) *reinterpret_cast<float2*>(po + D) = make_float2(rt.m * a.scale_log2, rt.l);
     }
 }
-template <int D>
-__device__ inline void write_result(const VerifyArgs& a, const uint32_t* s_rows, const Item& it,
-                                    const RowTile<D>& rt, int u, int q) {
-    if (!RI_OK(rt.ri)) return;
-    write_result_word<D>(a, it, rt, u, s_rows[u / a.group], q);
-}
-
 template <int D>
 __device__ inline void sum_lane_groups(RowTile<D>& rt) {
     rt.l += __shfl_xor(rt.l, 16);
@@ -1044,8 +1047,6 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
 
 // ---------------------------------------------------------------- few rows
 
-constexpr int kMaxLoopsWG = 64;
-
 struct Job {
     int kind;              // 0 deep, 1 ring, 2 block
     int r;
@@ -1060,69 +1061,74 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
     constexpr int kMerge = 2 * RT * 16 * (D + 2);      // floats: merge buffers
     constexpr int kLds = (kStage * 2 > kMerge * 4) ? kStage * 2 : kMerge * 4;
     __shared__ __attribute__((aligned(16))) unsigned char s_raw[kLds];
-    __shared__ int s_loop[kMaxLoopsWG], s_imax[kMaxLoopsWG], s_blkjob[kMaxLoopsWG + 1];
-    __shared__ int s_nloops;
-    __shared__ uint32_t s_rows[kMaxRowsPerLaunch];
+    __shared__ int s_lw[4][64];                        // per wave: loop list
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, q = lane >> 4;
+    const int G = a.group;
+    // rows of the row block (sorted by loop, then block offset): row k_lo +
+    // lane in lane `lane` of w0, at most 16*RT/G + 1 of them; loaded before
+    // the sequence is known, so the two loads overlap
+    const int u_base = (int)((blockIdx.x >> 3) % a.nrb) * 16 * RT;
+    const int k_lo = u_base / G;
+    const int nk = min(a.rows_here, (min(a.M, u_base + 16 * RT) + G - 1) / G) - k_lo;
+    const uint32_t w0 = lane < nk ? a.rows[k_lo + lane] : 0u;
 
     Item it;
     if (!decode_item(a, it)) return;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n = lane & 15, q = lane >> 4;
-    const int G = a.group;
-    const int u_base = it.rb * 16 * RT;
-    stage_rows(a, s_rows);
-    __syncthreads();
+    // A wave's first tile is usually the deep tile at d0 + 32*wave: request it
+    // now, before the row-dependent set-up (clamped into the sequence's deep
+    // rows; reloaded below if the wave's first job is another tile).
+    const int d0 = (int)((int64_t)it.c * a.cl);
+    const int64_t dreg = ((int64_t)it.b * a.Hkv + it.g) * a.CP * D;
+    const int spec_base = (int)min((int64_t)d0 + 32 * wave, a.CP - 32);
+    Frags<D> f;
+    load_frags<D>(a.deep_k + dreg + (int64_t)spec_base * D, a.deep_v + dreg + (int64_t)spec_base * D, f, n, q);
     uint16_t* const sk = reinterpret_cast<uint16_t*>(s_raw) + wave * 2 * 32 * D;
     uint16_t* const sv = sk + 32 * D;
     float (*s_st)[RT][16][D + 2] = reinterpret_cast<float (*)[RT][16][D + 2]>(s_raw);
 
-    RowTile<D> rt[RT];
-    int E = 0;
+    // deep extent of the workgroup: the largest e_row of its rows
+    const int rr = (w0 >> 8) & 255, ii = w0 & 255;
+    const int E = wave_max(lane < nk ? e_row(a, it.L, ii, rr) : 0);
+    // loops of the row block, ascending: loop p in lane p of lw as r | imax << 8
+    // (a loop's rows are sorted by offset, so its last row has the largest);
+    // every wave builds the list itself, in its own LDS row
+    const int rprev = __shfl(rr, (lane + 63) & 63), rnext = __shfl(rr, (lane + 1) & 63);
+    const bool first = lane < nk && (lane == 0 || rprev != rr);
+    const bool lastr = lane < nk && (lane + 1 == nk || rnext != rr);
+    const uint64_t fmask = __ballot(first);
+    const int nloops = __popcll(fmask);
+    if (lastr) s_lw[wave][__popcll(fmask & ((2ull << lane) - 1)) - 1] = rr | (ii << 8);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int lw = lane < nloops ? s_lw[wave][lane] : 0;
+    const int loop_r = lw & 255;
+    // draft-block tiles of loops 0..p (inclusive running sum in lane p)
+    int bend = lane < nloops ? (lw >> 8) / 32 + 1 : 0;
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-        init_row<D>(a, s_rows, it, u_base + 16 * t + n, q, rt[t]);
-        if (RI_OK(rt[t].ri)) E = max(E, rt[t].e);
+    for (int o = 1; o < 64; o <<= 1) {
+        const int x = __shfl_up(bend, o);
+        if (lane >= o) bend += x;
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) E = max(E, __shfl_xor(E, o));
-    E = __builtin_amdgcn_readfirstlane(E);
+    // loops are ascending and R is the largest, so the loops r < R are the
+    // first n_ring_planes of the list
+    const bool has_R = nloops > 0 && __builtin_amdgcn_readlane(loop_r, nloops - 1) == a.R;
+    const int n_ring_planes = nloops - (has_R ? 1 : 0);
 
-    const int k_lo = u_base / G;
-    const int k_hi = min(a.rows_here, (min(a.M, u_base + 16 * RT) + G - 1) / G);
-    if (threadIdx.x == 0) {
-        int nl = 0, prev = -1;
-        for (int k = k_lo; k < k_hi; ++k) {
-            const uint32_t rw = s_rows[k];
-            const int rr = (rw >> 8) & 255, ii = rw & 255;
-            if (rr != prev) {
-                s_loop[nl] = rr;
-                s_imax[nl] = ii;
-                ++nl;
-                prev = rr;
-            } else {
-                s_imax[nl - 1] = max(ii, s_imax[nl - 1]);
-            }
-        }
-        s_blkjob[0] = 0;
-        for (int p = 0; p < nl; ++p) s_blkjob[p + 1] = s_blkjob[p] + (s_imax[p] + 32) / 32;
-        s_nloops = nl;
-    }
-    __syncthreads();
-    const int nloops = s_nloops;
-    const int d0 = (int)((int64_t)it.c * a.cl);
     const int d1 = (int)min((int64_t)d0 + a.cl, (int64_t)E);
     const int n_deep = d1 > d0 ? (d1 - d0 + 31) / 32 : 0;
     const int ring_tiles = (it.last && a.R > 1 && it.nsl > 0) ? (it.nsl + 31) / 32 : 0;
-    int n_ring_planes = 0;
-    if (ring_tiles > 0)
-        for (int p = 0; p < nloops; ++p) n_ring_planes += s_loop[p] < a.R;
     const int n_ring = n_ring_planes * ring_tiles;
-    const int n_block = it.last ? s_blkjob[nloops] : 0;
+    const int n_block = it.last ? __builtin_amdgcn_readlane(bend, 63) : 0;
     const int n_jobs = n_deep + n_ring + n_block;
-    const int64_t dreg = ((int64_t)it.b * a.Hkv + it.g) * a.CP * D;
     const int64_t rreg0 = ((int64_t)it.b * a.Hkv + it.g) * a.NR * a.WP * D;
     const float sl2 = a.scale_log2;
 
+    // job j of the workgroup (wave-uniform j): deep tiles, then ring tiles
+    // plane by plane, then draft-block tiles loop by loop
     auto job_of = [&](int j) -> Job {
         Job jb;
         if (j < n_deep) {
@@ -1136,13 +1142,8 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
         j -= n_deep;
         if (j < n_ring) {
             const int pl = j / ring_tiles, st = j % ring_tiles;
-            int p = 0, seen = -1;
-            for (; p < nloops; ++p) {
-                seen += s_loop[p] < a.R;
-                if (seen == pl) break;
-            }
             jb.kind = 1;
-            jb.r = s_loop[p];
+            jb.r = __builtin_amdgcn_readlane(loop_r, pl);
             jb.base = st * 32;
             const int64_t rreg = rreg0 + (int64_t)(jb.r - 1) * a.WP * D;
             jb.K = a.ring_k + rreg + (int64_t)jb.base * D;
@@ -1150,28 +1151,53 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
             return jb;
         }
         j -= n_ring;
-        int p = 0;
-        while (s_blkjob[p + 1] <= j) ++p;
+        const int p = (int)__builtin_ctzll(__ballot(lane < nloops && bend > j));
         jb.kind = 2;
-        jb.r = s_loop[p];
-        jb.base = (j - s_blkjob[p]) * 32;
+        jb.r = __builtin_amdgcn_readlane(loop_r, p);
+        jb.base = (j - (p > 0 ? __builtin_amdgcn_readlane(bend, p - 1) : 0)) * 32;
         jb.K = a.bk.p + it.b * a.bk.sb + (int64_t)(jb.r - 1) * a.bk.sp + it.g * a.bk.sh;
         jb.V = a.bv.p + it.b * a.bv.sb + (int64_t)(jb.r - 1) * a.bv.sp + it.g * a.bv.sh;
         return jb;
     };
+
+    // Committed tiles (deep, ring) are read from HBM in the operand order
+    // straight into registers.  Where the registers allow (kAhead), one tile
+    // ahead: a wave loads the operands of its next committed tile before it
+    // computes the current one.  Those loads are unconditional (past its last
+    // committed tile a wave reloads the first deep tile and ignores it), so
+    // the compiler counts them exactly.
+    constexpr bool kAhead = D * RT <= 128;
+    const int n_comm = n_deep + n_ring;
+    auto comm_load = [&](int j, Frags<D>& f) {
+        const uint16_t* K = a.deep_k + dreg;
+        const uint16_t* V = a.deep_v + dreg;
+        if (j < n_comm) {
+            const Job jb = job_of(j);
+            K = jb.K;
+            V = jb.V;
+        }
+        load_frags<D>(K, V, f, n, q);
+    };
+    if (wave >= n_deep) comm_load(wave, f);
+    RowTile<D> rt[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int u = u_base + 16 * t + n;
+        init_row_word<D>(a, it, u, __shfl(w0, u < a.M ? u / G - k_lo : 0), q, rt[t]);
+    }
 
     for (int j = wave; j < n_jobs; j += 4) {
         const Job jb = job_of(j);
         const int kind = __builtin_amdgcn_readfirstlane(jb.kind);
         const int jr = __builtin_amdgcn_readfirstlane(jb.r);
         const int base = __builtin_amdgcn_readfirstlane(jb.base);
-        Frags<D> f;
+        Frags<D> fn;
+        if (kAhead) comm_load(j + 4, fn);
+        else if (kind != 2 && j != wave) comm_load(j, f);
         if (kind == 2) {
             stage_block<D>(a, jb.K, jb.V, base, sk, sv, lane);
             load_frags<D>(sk, sv, f, n, q);
             __builtin_amdgcn_wave_barrier();
-        } else {
-            load_frags<D>(jb.K, jb.V, f, n, q);
         }
 #pragma unroll
         for (int tr = 0; tr < RT; ++tr) {
@@ -1182,6 +1208,7 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
             else mode = mask_block<D>(rt[tr], jr, base, q, v);
             if (mode) tile_update<D>(rt[tr], f, mode == 2, v, sl2);
         }
+        if (kAhead) f = fn;
     }
 
     // merge the four waves' states: (2,3) -> (0,1) -> 0
@@ -1226,13 +1253,19 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
     if (wave != 0) return;
     take(0);
 #pragma unroll
-    for (int tr = 0; tr < RT; ++tr) write_result<D>(a, s_rows, it, rt[tr], u_base + 16 * tr + n, q);
+    for (int tr = 0; tr < RT; ++tr) {
+        const int u = u_base + 16 * tr + n;
+        write_result_word<D>(a, it, rt[tr], u, __shfl(w0, u < a.M ? u / G - k_lo : 0), q);
+    }
 }
 
 // ---------------------------------------------------------------- combine
 
 // Merge the chunk partials of every row-head of multi-chunk sequences:
 // M = max m_c, l = sum l_c 2^(m_c - M), O = sum O_c 2^(m_c - M) / l.
+// One wave per row-head.  Lane c reads the (m, l) of chunk c, so the chunk
+// states arrive together; the value rows of eight chunks are loaded before
+// any is summed, so the loads overlap instead of forming a chain.
 template <int D>
 __global__ void __launch_bounds__(256) k_combine(VerifyArgs a) {
     const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1243,26 +1276,47 @@ __global__ void __launch_bounds__(256) k_combine(VerifyArgs a) {
     const int bg = (int)(idx / a.M);
     const int g = bg % a.Hkv, b = bg / a.Hkv;
     const int64_t L = a.lens[b];
-    const int nc_b = L > 0 ? (int)((L + a.cl - 1) / a.cl) : 1;
+    const int nc_b = L > 0 ? (int)((L + a.cx + a.cl - 1) / a.cl) : 1;
     if (nc_b == 1) return;
-    const float* base = a.part + ((int64_t)bg * a.nc) * a.M * (D + 2);
+    const int64_t cs = (int64_t)a.M * (D + 2);                  // chunk stride
+    const float* pu = a.part + (int64_t)bg * a.nc * cs + (int64_t)u * (D + 2);
     float mx = -INFINITY;
-    for (int c = 0; c < nc_b; ++c) mx = fmaxf(mx, base[((int64_t)c * a.M + u) * (D + 2) + D]);
-    float lt = 0.f;
+    for (int c = lane; c < nc_b; c += 64) mx = fmaxf(mx, pu[c * cs + D]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     constexpr int NE = (D + 63) / 64;
-    float acc[NE];
+    constexpr int CB = 8;                                          // chunks per batch of loads
+    float acc[NE], lt = 0.f;
 #pragma unroll
     for (int t = 0; t < NE; ++t) acc[t] = 0.f;
-    for (int c = 0; c < nc_b; ++c) {
-        const float* p = base + ((int64_t)c * a.M + u) * (D + 2);
-        const float w = p[D] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(p[D] - mx);
-        lt += w * p[D + 1];
+    for (int c0 = 0; c0 < nc_b; c0 += 64) {
+        float w = 0.f;
+        if (c0 + lane < nc_b) {
+            const float* p = pu + (c0 + lane) * cs;
+            const float m = p[D];
+            w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mx);
+            lt += w * p[D + 1];
+        }
+        const int n = min(64, nc_b - c0);
+        for (int k = 0; k < n; k += CB) {
+            float v[CB][NE];
 #pragma unroll
-        for (int t = 0; t < NE; ++t) {
-            const int e = lane + 64 * t;
-            if (e < D) acc[t] += w * p[e];
+            for (int j = 0; j < CB; ++j)
+#pragma unroll
+                for (int t = 0; t < NE; ++t) {
+                    const int e = lane + 64 * t;
+                    v[j][t] = (k + j < n && e < D) ? pu[(c0 + k + j) * cs + e] : 0.f;
+                }
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                const float wj = __shfl(w, k + j);
+#pragma unroll
+                for (int t = 0; t < NE; ++t) acc[t] += wj * v[j][t];
+            }
         }
     }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) lt += __shfl_xor(lt, o);
     const uint32_t rw = a.rows[u / a.group];
     const int orig = (int)(rw >> 16), h = g * a.group + u % a.group;
     float* op = a.out + (((int64_t)b * a.n_rows + orig) * a.Hq + h) * D;
