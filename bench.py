@@ -59,6 +59,10 @@ def parse():
                          "R calls of D rows (per-loop), or the draft pass of D x r_draft "
                          "single-row calls (draft)")
     ap.add_argument("--draft-loops", type=int, default=4, help="r_draft of the draft pass")
+    ap.add_argument("--capacity-gib", type=float, default=0.0, metavar="GIB",
+                    help="fixed-memory mode: for a cache budget of GIB GiB, the batch each "
+                         "layout holds (full, RIPE, deepest plane) and the verify throughput "
+                         "measured at that batch")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -179,6 +183,101 @@ def cpu_baseline(wl, window, anchor, calls):
             "tokens_per_s": round(wl.batch * len({i for i, _ in rows}) * rounds / spent, 3)}
 
 
+def capacity_bench(args):
+    """Batch capacity at fixed memory, fed with measured verify times.
+
+    For a cache budget, each layout (the full per-loop cache, RIPE with window
+    W, the deepest plane alone) holds ripe_max_batch sequences of the
+    workload's shape; the verify call of one layer is timed at that batch
+    (layers are alike, so a step of n_layers calls takes n_layers times as
+    long) and the verified tokens per second of the attention alone are
+    reported per layout.  Every sequence holds the same synthetic prefix
+    (timing does not depend on the values; parity is covered by the tests).
+    """
+    import torch
+    import ripe_harness as H
+    from self_speculative_verify_amd import RipeCache, ripe
+    from synth import WINDOW_FULL, named_workload
+
+    wl = named_workload(args.workload)
+    if args.workload == "wave" or len(set(wl.lens)) != 1:
+        print("--capacity-gib needs a workload with one length and the D x R grid", file=sys.stderr)
+        sys.exit(2)
+    L, D, R = wl.lens[0], wl.n_blk, wl.n_loops
+    w_ripe = args.window if args.window is not None else (wl.window if wl.window not in (0, WINDOW_FULL) else 64)
+    budget = int(args.capacity_gib * (1 << 30))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows = wl.rows
+    out = {}
+    for name, W in (("full", WINDOW_FULL), ("ripe", w_ripe), ("deepest", 0)):
+        cfg = ripe.config(wl.n_layers, R, wl.n_heads_q, wl.n_heads_kv, wl.head_dim, W, 1,
+                          wl.capacity, wl.max_block, wl.anchor)
+        B = ripe.ripe_max_batch(cfg, budget)
+        if B < 1:
+            out[name] = {"window": "full" if W == WINDOW_FULL else W, "batch": 0}
+            continue
+        print(f"capacity: {name} W={W} batch {B}", file=sys.stderr, flush=True)
+        cfg.batch = B
+        per_seq = (ripe.ripe_cache_bytes(cfg) - ripe.ripe_cache_bytes(
+            ripe.config(wl.n_layers, R, wl.n_heads_q, wl.n_heads_kv, wl.head_dim, W, 1,
+                        wl.capacity, wl.max_block, wl.anchor))) / max(B - 1, 1)
+        cache = RipeCache(1, R, wl.n_heads_q, wl.n_heads_kv, wl.head_dim, W, B, wl.capacity,
+                          wl.max_block, wl.anchor, device=dev)
+        nw = 0 if R == 1 else min(L, cache.cfg.window, wl.capacity)
+        dk, dv, wk, wv = wl.prefix(0, 0, n_win=nw)
+        Hk, d = wl.n_heads_kv, wl.head_dim
+        tk = H.to_dev(dk, dev).view(1, Hk, L, d).expand(B, Hk, L, d)
+        tv = H.to_dev(dv, dev).view(1, Hk, L, d).expand(B, Hk, L, d)
+        twk = twv = None
+        if nw > 0:
+            twk = H.to_dev(wk, dev).view(1, R - 1, Hk, nw, d).expand(B, R - 1, Hk, nw, d)
+            twv = H.to_dev(wv, dev).view(1, R - 1, Hk, nw, d).expand(B, R - 1, Hk, nw, d)
+        cache.append(0, [L] * B, tk, tv, twk, twv)
+        del tk, tv, twk, twv
+        q = torch.randn((B, len(rows), wl.n_heads_q, d), device=dev).to(torch.bfloat16)
+        bk1, bv1 = wl.block(0)
+        bk = H.to_dev(bk1[:1], dev).expand(B, *bk1.shape[1:])
+        bv = H.to_dev(bv1[:1], dev).expand(B, *bv1.shape[1:])
+        o = torch.empty((B, len(rows), wl.n_heads_q, d), device=dev)
+        lse = torch.empty((B, len(rows), wl.n_heads_q), device=dev)
+        for _ in range(max(2, args.warmup // 2)):
+            cache.verify(0, rows, q, bk, bv, D, out=o, lse=lse)
+        torch.cuda.synchronize()
+        n = max(3, args.steps // 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            cache.verify(0, rows, q, bk, bv, D, out=o, lse=lse)
+        e1.record()
+        torch.cuda.synchronize()
+        t_layer = e0.elapsed_time(e1) / n / 1e3
+        u = unique_kv_bytes(wl, W, wl.anchor, rows, [L] * B)
+        out[name] = {"window": "full" if W == WINDOW_FULL else W, "batch": B,
+                     "cache_bytes": int(ripe.ripe_cache_bytes(cfg)),
+                     "bytes_per_sequence": int(per_seq),
+                     "us_per_layer": round(t_layer * 1e6, 2),
+                     "GB/s": round(u / t_layer / 1e9, 1),
+                     "tokens_per_s": round(B * D / (wl.n_layers * t_layer), 1)}
+        del cache, q, o, lse, bk, bv
+        torch.cuda.empty_cache()
+    full_tps = out["full"].get("tokens_per_s") or None
+    res = {
+        "metric": "verified tokens/s of the attention at fixed cache memory (batch = what fits)",
+        "value": out["ripe"].get("tokens_per_s", 0.0), "unit": "tokens/s", "n_gpus": 1,
+        "steps": max(3, args.steps // 2), "warmup": max(2, args.warmup // 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "budget_gib": args.capacity_gib, "layers": wl.n_layers,
+                   "loops": R, "heads_q": wl.n_heads_q, "heads_kv": wl.n_heads_kv,
+                   "head_dim": wl.head_dim, "context": L, "block": D, "timed_layers": 1},
+        "layouts": out,
+        "ripe_vs_full": round(out["ripe"]["tokens_per_s"] / full_tps, 3) if full_tps and "tokens_per_s" in out["ripe"] else None,
+        "deepest_vs_full": round(out["deepest"]["tokens_per_s"] / full_tps, 3) if full_tps and "tokens_per_s" in out["deepest"] else None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -186,6 +285,9 @@ def main():
               "(the verification path is data-parallel over sequences and KV heads and "
               "needs no collective; run one process per GPU).", file=sys.stderr)
         sys.exit(2)
+    if args.capacity_gib > 0:
+        capacity_bench(args)
+        return
     import torch
     import ripe_harness as H
     from synth import WINDOW_FULL, named_workload

@@ -122,6 +122,18 @@ size_t ripe_cache_bytes(const ripe_config* cfg);
 int64_t ripe_section_offset(const ripe_config* cfg, int32_t section);
 
 /*
+ * Batch capacity at fixed memory: the largest batch B in [1, 4096] whose
+ * storage, ripe_cache_bytes of cfg with its batch field set to B, fits in
+ * budget_bytes; 0 if not even one sequence fits; -1 if cfg is invalid (its
+ * batch field is ignored).  RIPE's memory saving (abstract, fourth and fifth
+ * sentences) read as sequences per budget: with capacity C and the window
+ * rounded up to a multiple of 32, a recurrent layer stores C + W(R - 1)
+ * vectors per sequence instead of R*C, or C with the deepest plane alone
+ * (W = 0).  Host arithmetic only.
+ */
+int32_t ripe_max_batch(const ripe_config* cfg, size_t budget_bytes);
+
+/*
  * Bind a handle to caller-owned storage of at least ripe_cache_bytes(cfg)
  * bytes (device memory, 256-byte aligned) and zero-fill it on `stream`.
  * All lengths start at 0.  The storage must outlive the handle.

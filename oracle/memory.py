@@ -8,6 +8,12 @@ per-loop cache.  Counting stored (position, plane) vectors per layer:
   full cache, recurrent layer  : R * L
   RIPE,       recurrent layer  : L + min(W, L) * (R - 1)
   any non-recurrent layer      : L (one plane)
+
+A vector is a key and a value of all KV heads in bf16 (4 * Hkv * d bytes), so
+a sequence's bytes are the vector count times that, and a memory budget holds
+floor(budget / bytes per sequence) sequences: the batch capacity at fixed
+memory, for the full cache (W >= L), RIPE (window W) and the deepest plane
+alone (W = 0).
 """
 from __future__ import annotations
 
@@ -23,3 +29,19 @@ def ripe_vectors(L: int, W: int, R: int, n_recurrent: int, n_plain: int = 0) -> 
 def ripe_fraction(L: int, W: int, R: int, n_recurrent: int, n_plain: int = 0) -> float:
     """RIPE memory as a fraction of the full per-loop cache."""
     return ripe_vectors(L, W, R, n_recurrent, n_plain) / full_vectors(L, R, n_recurrent, n_plain)
+
+
+def vector_bytes(n_heads_kv: int, head_dim: int) -> int:
+    """Key and value of one (position, loop) for all KV heads, bf16."""
+    return 2 * n_heads_kv * head_dim * 2
+
+
+def sequence_bytes(L: int, W: int, R: int, n_heads_kv: int, head_dim: int,
+                   n_recurrent: int, n_plain: int = 0) -> int:
+    """Cache bytes of one sequence holding L positions (W >= L: full cache)."""
+    return ripe_vectors(L, W, R, n_recurrent, n_plain) * vector_bytes(n_heads_kv, head_dim)
+
+
+def max_batch(budget_bytes: int, per_sequence_bytes: int) -> int:
+    """Sequences a memory budget holds."""
+    return budget_bytes // per_sequence_bytes

@@ -212,6 +212,22 @@ int64_t ripe_section_offset(const ripe_config* cfg, int32_t section) {
     return -1;
 }
 
+int32_t ripe_max_batch(const ripe_config* cfg, size_t budget_bytes) {
+    if (!cfg) return -1;
+    ripe_config c = *cfg;
+    c.batch = 1;
+    if (!valid_config(&c)) return -1;
+    // storage grows with the batch: bisect for the last batch that fits
+    int32_t lo = 0, hi = 4096;
+    while (lo < hi) {
+        const int32_t mid = lo + (hi - lo + 1) / 2;
+        c.batch = mid;
+        if (valid_config(&c) && (size_t)geometry(&c).total <= budget_bytes) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
 ripe_status ripe_cache_create(const ripe_config* cfg, void* d_storage, size_t bytes,
                               hipStream_t stream, ripe_cache** out) {
     if (!out) return RIPE_EINVAL;

@@ -18,7 +18,7 @@ __all__ = [
     "RIPE_SECTION_LENS", "RIPE_SECTION_DEEP_K", "RIPE_SECTION_DEEP_V",
     "RIPE_SECTION_RING_K", "RIPE_SECTION_RING_V", "RIPE_SECTION_END",
     "RipeConfig", "RipeKVView", "RipeError", "library_path", "load",
-    "ripe_cache_bytes", "ripe_section_offset", "ripe_cache_create", "ripe_destroy",
+    "ripe_cache_bytes", "ripe_section_offset", "ripe_max_batch", "ripe_cache_create", "ripe_destroy",
     "ripe_get_lengths", "ripe_append", "ripe_workspace_bytes", "ripe_verify_attn",
     "ripe_status_string", "kv_view", "null_view", "config",
 ]
@@ -68,6 +68,8 @@ def load():
         L.ripe_cache_bytes.argtypes = [CFG]
         L.ripe_section_offset.restype = I64
         L.ripe_section_offset.argtypes = [CFG, I32]
+        L.ripe_max_batch.restype = I32
+        L.ripe_max_batch.argtypes = [CFG, SZ]
         L.ripe_cache_create.restype = I32
         L.ripe_cache_create.argtypes = [CFG, P, SZ, P, ctypes.POINTER(P)]
         L.ripe_destroy.restype = None
@@ -137,6 +139,11 @@ def ripe_cache_bytes(cfg: RipeConfig) -> int:
 
 def ripe_section_offset(cfg: RipeConfig, section: int) -> int:
     return int(load().ripe_section_offset(ctypes.byref(cfg), int(section)))
+
+
+def ripe_max_batch(cfg: RipeConfig, budget_bytes: int) -> int:
+    """Largest batch whose storage fits in budget_bytes (0: none; -1: invalid)."""
+    return int(load().ripe_max_batch(ctypes.byref(cfg), int(budget_bytes)))
 
 
 def ripe_cache_create(cfg: RipeConfig, storage: torch.Tensor, stream=None) -> ctypes.c_void_p:
