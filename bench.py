@@ -54,11 +54,15 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graphs")
-    ap.add_argument("--mode", default="batched", choices=["batched", "per-loop", "draft"],
+    ap.add_argument("--mode", default="batched", choices=["batched", "per-loop", "draft", "wavefront"],
                     help="call schedule: the D x R grid in one call per layer (batched), "
                          "R calls of D rows (per-loop), or the draft pass of D x r_draft "
                          "single-row calls (draft)")
     ap.add_argument("--draft-loops", type=int, default=4, help="r_draft of the draft pass")
+    ap.add_argument("--accept", type=float, default=0.8,
+                    help="wavefront: probability that a draft token is accepted (seeded)")
+    ap.add_argument("--shared-kv", action="store_true",
+                    help="wavefront: one KV plane shared by all loops")
     ap.add_argument("--capacity-gib", type=float, default=0.0, metavar="GIB",
                     help="fixed-memory mode: for a cache budget of GIB GiB, the batch each "
                          "layout holds (full, RIPE, deepest plane) and the verify throughput "
@@ -278,6 +282,118 @@ def capacity_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def wavefront_bench(args):
+    """WaveFront decoding of one sequence: every call verifies the positions in
+    flight (one row each, at its own loop) in each layer; a position that
+    reaches full depth is appended to every layer's cache; drafts are accepted
+    with a seeded probability.  Timed: `steps` calls (at least 16R) after
+    `warmup` calls, attention and commit appends only (the model's planes are
+    not written; values do not change the timing).  The autoregressive
+    baseline runs R single-row calls per token."""
+    import numpy as np
+    import torch
+    import ripe_harness as H
+    from self_speculative_verify_amd import RipeCache
+    from self_speculative_verify_amd.wavefront import (WaveBuffer, WaveScheduler,
+                                                       expected_calls_per_token, kernel_rows)
+    from synth import named_workload
+
+    wl = named_workload(args.workload)
+    if wl.batch != 1:
+        print("--mode wavefront runs one sequence; pick a workload with batch 1", file=sys.stderr)
+        sys.exit(2)
+    R, L = wl.n_loops, wl.lens[0]
+    rd = min(args.draft_loops, R - 1)
+    width = -(-R // rd)
+    shared = args.shared_kv
+    R_store = 1 if shared else R
+    window = wl.window if args.window is None else args.window
+    n_calls = max(args.steps, 16 * R)
+    n_warm = max(args.warmup, 0)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.replace(n_loops=R_store, capacity=L + n_calls + n_warm + 2 * R + width, max_block=width)
+    cache = RipeCache(w.n_layers, R_store, w.n_heads_q, w.n_heads_kv, w.head_dim, window, 1,
+                      w.capacity, width, w.anchor, device=dev)
+    H.load_prefix(cache, w, device=dev)
+    buf = WaveBuffer(1, R_store, w.n_heads_kv, w.head_dim, slots=4 * width, device=dev)
+    buf.k.normal_()
+    buf.v.normal_()
+    q = torch.randn((1, width, w.n_heads_q, w.head_dim), device=dev).to(torch.bfloat16)
+    o = torch.empty((1, width, w.n_heads_q, w.head_dim), device=dev)
+    lse = torch.empty((1, width, w.n_heads_q), device=dev)
+    sched = WaveScheduler(R, rd, L)
+    buf.push()
+    rng = np.random.default_rng(np.random.SeedSequence([2024, int(args.accept * 1000)]))
+    u_total = 0
+
+    def call():
+        nonlocal u_total
+        rows = sched.rows()
+        krows = kernel_rows(rows, shared)
+        n = len(rows)
+        bk, bv = buf.block()
+        for layer in range(w.n_layers):
+            cache.verify(layer, krows, q[:, :n], bk, bv, n, out=o[:, :n], lse=lse[:, :n])
+        u_total += w.n_layers * unique_kv_bytes(w, window, w.anchor, krows, [sched.L])
+        ev = sched.after_call(lambda: bool(rng.random() < args.accept))
+        if ev.committed is not None:
+            planes = buf.oldest_planes()
+            for layer in range(w.n_layers):
+                cache.append(layer, [1], *planes)
+            buf.pop_oldest()
+        if ev.rejected:
+            buf.reset(0)
+        while buf.count < sched.width:
+            buf.push()
+
+    for _ in range(n_warm):
+        call()
+    torch.cuda.synchronize()
+    c0, k0 = sched.calls, sched.commits
+    u_total = 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3
+    commits = sched.commits - k0
+
+    # autoregressive baseline: R single-row calls per token (every layer)
+    n_tok = 2
+    e0.record()
+    for _ in range(n_tok):
+        for r in range(1, R + 1):
+            kr = kernel_rows([(0, r)], shared)
+            for layer in range(w.n_layers):
+                bk, bv = buf.block()
+                cache.verify(layer, kr, q[:, :1], bk, bv, 1, out=o[:, :1], lse=lse[:, :1])
+    e1.record()
+    torch.cuda.synchronize()
+    t_ar = e0.elapsed_time(e1) / 1e3 / n_tok
+    tps = commits / t
+    res = {
+        "metric": "WaveFront decoding: committed tokens/s of the attention and commit appends",
+        "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": n_calls,
+        "warmup": n_warm, "ms_per_step": round(t / n_calls * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "layers": w.n_layers, "loops": R, "draft_loops": rd,
+                   "wave_width": width, "shared_kv": shared, "accept": args.accept,
+                   "window": window, "heads_q": w.n_heads_q, "heads_kv": w.n_heads_kv,
+                   "head_dim": w.head_dim, "context": L},
+        "calls": n_calls, "commits": commits,
+        "calls_per_token": round(n_calls / max(commits, 1), 3),
+        "expected_calls_per_token": round(expected_calls_per_token(R, rd, args.accept), 3),
+        "us_per_call": round(t / n_calls * 1e6, 2),
+        "unique_kv_GB_per_s": round(u_total / t / 1e9, 1),
+        "autoregressive_tokens_per_s": round(1 / t_ar, 1),
+        "speedup_vs_autoregressive": round(tps * t_ar, 3),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -287,6 +403,9 @@ def main():
         sys.exit(2)
     if args.capacity_gib > 0:
         capacity_bench(args)
+        return
+    if args.mode == "wavefront":
+        wavefront_bench(args)
         return
     import torch
     import ripe_harness as H
