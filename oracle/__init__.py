@@ -63,6 +63,10 @@ def lib():
         L.ora_verify.restype = ctypes.c_int32
         L.ora_verify.argtypes = [ctypes.POINTER(OraConfig), P, ctypes.c_int32, ctypes.c_int32,
                                  P, P, P, P, P, P, ctypes.c_int32, P, P, P]
+        L.ora_draft.restype = ctypes.c_int32
+        L.ora_draft.argtypes = [ctypes.POINTER(OraConfig), P, ctypes.c_int32, ctypes.c_int32,
+                                P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                P, P, P]
         L.ora_threads.restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -139,6 +143,16 @@ class OracleCache:
         q: uint16 [B][n_rows][Hq][d]; blk_k/blk_v: uint16 [B][R][Hkv][Dmax][d].
         Returns (out [B][n_rows][Hq][d], lse [B][n_rows][Hq]) as float64.
         """
+        return self._attend(layer, rows, q, blk_k, blk_v, n_blk, None, want)
+
+    def draft(self, layer: int, rows: Sequence[Tuple[int, int]], q: np.ndarray,
+              blk_k: np.ndarray, blk_v: np.ndarray, n_blk: int, n_sink: int, w_draft: int,
+              want: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """fp64 windowed draft attention: committed keys are the first n_sink
+        positions and the w_draft positions before the query."""
+        return self._attend(layer, rows, q, blk_k, blk_v, n_blk, (n_sink, w_draft), want)
+
+    def _attend(self, layer, rows, q, blk_k, blk_v, n_blk, window, want):
         c = self.cfg
         rb = np.ascontiguousarray([i for i, _ in rows], dtype=np.int32)
         rl = np.ascontiguousarray([r for _, r in rows], dtype=np.int32)
@@ -152,11 +166,16 @@ class OracleCache:
         out = np.zeros((c.batch, nr, c.n_heads_q, c.head_dim), dtype=np.float64)
         lse = np.zeros((c.batch, nr, c.n_heads_q), dtype=np.float64)
         w = None if want is None else np.ascontiguousarray(want, dtype=np.uint8)
-        st = lib().ora_verify(ctypes.byref(c), _ptr(self.image), layer, nr, _ptr(rb), _ptr(rl),
-                              _ptr(q), _ptr(bk), _ptr(bv), _ptr(bs), n_blk, _ptr(w),
-                              _ptr(out), _ptr(lse))
+        if window is None:
+            st = lib().ora_verify(ctypes.byref(c), _ptr(self.image), layer, nr, _ptr(rb), _ptr(rl),
+                                  _ptr(q), _ptr(bk), _ptr(bv), _ptr(bs), n_blk, _ptr(w),
+                                  _ptr(out), _ptr(lse))
+        else:
+            st = lib().ora_draft(ctypes.byref(c), _ptr(self.image), layer, nr, _ptr(rb), _ptr(rl),
+                                 _ptr(q), _ptr(bk), _ptr(bv), _ptr(bs), n_blk, int(window[0]),
+                                 int(window[1]), _ptr(w), _ptr(out), _ptr(lse))
         if st != ORA_OK:
-            raise RuntimeError(f"oracle verify failed with status {st}")
+            raise RuntimeError(f"oracle attention failed with status {st}")
         return out, lse
 
 

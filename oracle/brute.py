@@ -56,8 +56,12 @@ class BruteCache:
     def entries(self, b: int, g: int) -> int:
         return sum(1 for k in self.store if k[0] == b and k[1] == g)
 
-    def verify_one(self, b: int, i: int, r: int, h: int, q, blk_k, blk_v) -> Tuple[np.ndarray, float]:
-        """q: uint16 [d]; blk_*: uint16 [R][H][Dmax][d] of sequence b."""
+    def verify_one(self, b: int, i: int, r: int, h: int, q, blk_k, blk_v,
+                   sink_window=None) -> Tuple[np.ndarray, float]:
+        """q: uint16 [d]; blk_*: uint16 [R][H][Dmax][d] of sequence b.
+        sink_window = (n_sink, w): a windowed draft row keeps only the committed
+        positions s < n_sink or s >= L + i - w (page "Windowed-MTP", abstract:
+        sliding window plus attention sink on the draft's attention)."""
         L = self.lens[b]
         t = L + i
         beta = t - self.W if self.anchor == 0 else L - self.W
@@ -65,6 +69,8 @@ class BruteCache:
         qf = [float(x) for x in bf16_to_f32(q)]
         keys, vals = [], []
         for s in range(t + 1):
+            if s < L and sink_window is not None and not (s < sink_window[0] or s >= t - sink_window[1]):
+                continue
             if s >= L:
                 k, v = blk_k[r - 1, g, s - L], blk_v[r - 1, g, s - L]
             else:
@@ -84,7 +90,7 @@ class BruteCache:
                 out[e] += w * vv[e]
         return out, m + math.log(z)
 
-    def verify(self, rows: Sequence[Tuple[int, int]], q, blk_k, blk_v):
+    def verify(self, rows: Sequence[Tuple[int, int]], q, blk_k, blk_v, sink_window=None):
         """q: uint16 [B][n_rows][Hq][d]; blk_*: uint16 [B][R][H][Dmax][d]."""
         out = np.zeros((self.B, len(rows), self.Hq, self.d))
         lse = np.zeros((self.B, len(rows), self.Hq))
@@ -92,5 +98,5 @@ class BruteCache:
             for k, (i, r) in enumerate(rows):
                 for h in range(self.Hq):
                     out[b, k, h], lse[b, k, h] = self.verify_one(b, i, r, h, q[b, k, h],
-                                                                 blk_k[b], blk_v[b])
+                                                                 blk_k[b], blk_v[b], sink_window)
         return out, lse

@@ -253,20 +253,35 @@ static int64_t plane_of(int64_t s, int64_t L, int64_t r, int64_t R, int64_t beta
 }
 
 /*
- * Verification attention for one layer.
+ * Is committed position s (< L) a key of a query at position t?  Every one is
+ * for verification (w_win < 0).  A windowed draft (page "Windowed-MTP:
+ * Removing the Full-Context Draft-KV Tax at Million-Token Context",
+ * abstract: a sliding window plus an attention sink on the draft's attention
+ * only) keeps the first n_sink positions and the positions s >= t - w_win.
+ */
+static int committed_key(int64_t s, int64_t t, int64_t n_sink, int64_t w_win) {
+    if (w_win < 0) return 1;
+    return s < n_sink || s >= t - w_win;
+}
+
+/*
+ * Attention for one layer.
  *   rows k = 0..n_rows-1 are (block offset row_blk[k], loop row_loop[k]);
  *   q      bf16 [B][n_rows][Hq][d];
  *   blk_k/blk_v: planes 1..R of the draft block, element (b, r-1, g, j, e)
  *          at b*bs[0] + (r-1)*bs[1] + g*bs[2] + j*bs[3] + e;
+ *   n_sink, w_win: the committed keys a query keeps (committed_key above);
  *   want   optional [B][n_rows][Hq] mask of the outputs to compute;
  *   out    double [B][n_rows][Hq][d], lse double [B][n_rows][Hq].
- * For each query: scores q.k/sqrt(d) over keys 0..L+i at the plane the rule
- * picks, LSE = M + ln sum exp(score - M), O = sum exp(score - LSE) v.
+ * For each query: scores q.k/sqrt(d) over its keys among 0..L+i (block keys
+ * L..L+i always) at the plane the rule picks, LSE = M + ln sum exp(score -
+ * M), O = sum exp(score - LSE) v.
  */
-int32_t ora_verify(const ora_config* c, const void* storage, int32_t layer, int32_t n_rows,
-                   const int32_t* row_blk, const int32_t* row_loop, const uint16_t* q,
-                   const uint16_t* blk_k, const uint16_t* blk_v, const int64_t* bs,
-                   int32_t n_blk, const uint8_t* want, double* out, double* lse) {
+static int32_t attend(const ora_config* c, const void* storage, int32_t layer, int32_t n_rows,
+                      const int32_t* row_blk, const int32_t* row_loop, const uint16_t* q,
+                      const uint16_t* blk_k, const uint16_t* blk_v, const int64_t* bs,
+                      int32_t n_blk, int64_t n_sink, int64_t w_win, const uint8_t* want,
+                      double* out, double* lse) {
     if (!config_ok(c) || !storage || layer < 0 || layer >= c->n_layers || n_rows < 0) return ORA_EINVAL;
     if (n_blk < 0 || n_blk > c->max_block) return ORA_EINVAL;
     for (int32_t k = 0; k < n_rows; ++k) {
@@ -308,6 +323,10 @@ int32_t ora_verify(const ora_config* c, const void* storage, int32_t layer, int3
         int st = ORA_OK;
         double M = -INFINITY;
         for (int64_t s = 0; s < n_keys && st == ORA_OK; ++s) {
+            if (s < L && !committed_key(s, t, n_sink, w_win)) {
+                sc[s] = -INFINITY;      /* not a key of this query */
+                continue;
+            }
             st = fetch(&x, b, g, L, s, plane_of(s, L, r, R, beta), 0, kvec);
             double acc = 0.0;
             for (int64_t e = 0; e < d; ++e) acc += qd[e] * kvec[e];
@@ -320,6 +339,7 @@ int32_t ora_verify(const ora_config* c, const void* storage, int32_t layer, int3
         double* o = out + idx * d;
         for (int64_t e = 0; e < d; ++e) o[e] = 0.0;
         for (int64_t s = 0; s < n_keys && st == ORA_OK; ++s) {
+            if (sc[s] == -INFINITY) continue;
             st = fetch(&x, b, g, L, s, plane_of(s, L, r, R, beta), 1, kvec);
             const double w = exp(sc[s] - l);
             for (int64_t e = 0; e < d; ++e) o[e] += w * kvec[e];
@@ -334,6 +354,27 @@ int32_t ora_verify(const ora_config* c, const void* storage, int32_t layer, int3
         free(sc);
     }
     return status;
+}
+
+/* Verification attention: every committed position is a key. */
+int32_t ora_verify(const ora_config* c, const void* storage, int32_t layer, int32_t n_rows,
+                   const int32_t* row_blk, const int32_t* row_loop, const uint16_t* q,
+                   const uint16_t* blk_k, const uint16_t* blk_v, const int64_t* bs,
+                   int32_t n_blk, const uint8_t* want, double* out, double* lse) {
+    return attend(c, storage, layer, n_rows, row_blk, row_loop, q, blk_k, blk_v, bs, n_blk,
+                  0, -1, want, out, lse);
+}
+
+/* Windowed draft attention: committed keys are the first n_sink positions
+ * and the w_draft positions before the query (s >= L + i - w_draft). */
+int32_t ora_draft(const ora_config* c, const void* storage, int32_t layer, int32_t n_rows,
+                  const int32_t* row_blk, const int32_t* row_loop, const uint16_t* q,
+                  const uint16_t* blk_k, const uint16_t* blk_v, const int64_t* bs,
+                  int32_t n_blk, int32_t n_sink, int32_t w_draft, const uint8_t* want,
+                  double* out, double* lse) {
+    if (n_sink < 0 || w_draft < 0) return ORA_EINVAL;
+    return attend(c, storage, layer, n_rows, row_blk, row_loop, q, blk_k, blk_v, bs, n_blk,
+                  n_sink, w_draft, want, out, lse);
 }
 
 /* number of OpenMP threads the oracle will use (for reporting) */
