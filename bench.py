@@ -59,6 +59,10 @@ def parse():
                          "R calls of D rows (per-loop), or the draft pass of D x r_draft "
                          "single-row calls (draft)")
     ap.add_argument("--draft-loops", type=int, default=4, help="r_draft of the draft pass")
+    ap.add_argument("--draft-window", type=int, default=-1, metavar="W_D",
+                    help="draft mode: windowed draft attention keeping the W_D committed "
+                         "positions before each query and --sinks sink positions (-1: full)")
+    ap.add_argument("--sinks", type=int, default=4, help="sink positions of a windowed draft")
     ap.add_argument("--accept", type=float, default=0.8,
                     help="wavefront: probability that a draft token is accepted (seeded)")
     ap.add_argument("--shared-kv", action="store_true",
@@ -79,8 +83,11 @@ def key_range(L, i, r, R, window, anchor):
     return L if r == R else min(max(beta, 0), L)
 
 
-def unique_kv_bytes(wl, window, anchor, rows, lens):
-    """Distinct (position, loop) key and value vectors one layer's call reads."""
+def unique_kv_bytes(wl, window, anchor, rows, lens, sink_window=None):
+    """Distinct (position, loop) key and value vectors one layer's call reads
+    (sink_window = (n_sink, w): a windowed draft's committed keys only)."""
+    if sink_window is not None:
+        return _unique_windowed(wl, window, anchor, rows, lens, *sink_window)
     R, H, d = wl.n_loops, wl.n_heads_kv, wl.head_dim
     total = 0
     for L in lens:
@@ -94,6 +101,28 @@ def unique_kv_bytes(wl, window, anchor, rows, lens):
                 e_min[r] = min(e_min.get(r, L), e)
             blk[r] = max(blk.get(r, -1), i)
         total += e_max_R + sum(L - e for e in e_min.values()) + sum(i + 1 for i in blk.values())
+    return total * 2 * H * d * 2
+
+
+def _unique_windowed(wl, window, anchor, rows, lens, n_sink, w):
+    import numpy as np
+    R, H, d = wl.n_loops, wl.n_heads_kv, wl.head_dim
+    total = 0
+    for L in lens:
+        planes = {}                      # loop -> positions read at that loop
+        blk = {}
+        for i, r in rows:
+            e = key_range(L, i, r, R, window, anchor)
+            keep = np.zeros(L, dtype=bool)
+            keep[:min(n_sink, L)] = True
+            keep[max(L + i - w, 0):] = True
+            deep = planes.setdefault(R, np.zeros(L, dtype=bool))
+            deep[:e] |= keep[:e]
+            if e < L:
+                mine = planes.setdefault(r, np.zeros(L, dtype=bool))
+                mine[e:] |= keep[e:]
+            blk[r] = max(blk.get(r, -1), i)
+        total += sum(int(m.sum()) for m in planes.values()) + sum(i + 1 for i in blk.values())
     return total * 2 * H * d * 2
 
 
@@ -158,7 +187,7 @@ def time_append(wl, window, anchor, dev, n_rep):
             "GB/s": round(2 * moved / (us * 1e-6) / 1e9, 2), "tokens_per_seq": D}
 
 
-def cpu_baseline(wl, window, anchor, calls):
+def cpu_baseline(wl, window, anchor, calls, sw=None):
     """The fp64 oracle on whole layers of the workload (the same calls, every
     head), layer after layer until CPU_SAMPLE_S seconds are spent."""
     import numpy as np
@@ -172,9 +201,12 @@ def cpu_baseline(wl, window, anchor, calls):
         for c in calls:
             qc = np.ascontiguousarray(q[:, [wl.rows.index(x) for x in c.rows]])
             t0 = time.perf_counter()
-            oc.verify(layer, c.rows, qc, bk, bv, c.n_blk)
+            if sw is None:
+                oc.verify(layer, c.rows, qc, bk, bv, c.n_blk)
+            else:
+                oc.draft(layer, c.rows, qc, bk, bv, c.n_blk, sw[0], sw[1])
             spent += time.perf_counter() - t0
-            u += unique_kv_bytes(wl, window, anchor, c.rows, wl.lens)
+            u += unique_kv_bytes(wl, window, anchor, c.rows, wl.lens, sw)
         n_layers += 1
         del oc
         if spent >= CPU_SAMPLE_S:
@@ -432,7 +464,8 @@ def main():
     torch.cuda.set_device(dev)
 
     # algorithmic bytes and flops of one layer (all its calls)
-    u_calls = [unique_kv_bytes(wl, window, anchor, c.rows, wl.lens) for c in calls]
+    sw = (args.sinks, args.draft_window) if args.mode == "draft" and args.draft_window >= 0 else None
+    u_calls = [unique_kv_bytes(wl, window, anchor, c.rows, wl.lens, sw) for c in calls]
     f_calls = [flops(wl, c.rows, wl.lens) for c in calls]
     u_layer, f_layer = sum(u_calls), sum(f_calls)
     u_round = u_layer * wl.n_layers
@@ -470,8 +503,12 @@ def main():
         cache, ins, outs = setup
         qs, bk, bv = ins[layer]
         c = calls[k]
-        cache.verify(layer, c.rows, qs[k], bk, bv, c.n_blk, out=outs[layer][k][0],
-                     lse=outs[layer][k][1])
+        if sw is not None:
+            cache.draft(layer, c.rows, qs[k], bk, bv, c.n_blk, sw[0], sw[1], out=outs[layer][k][0],
+                        lse=outs[layer][k][1])
+        else:
+            cache.verify(layer, c.rows, qs[k], bk, bv, c.n_blk, out=outs[layer][k][0],
+                         lse=outs[layer][k][1])
 
     def run_round(setup):
         # the order a forward pass runs: call by call (loop by loop), each
@@ -562,7 +599,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(wl, window, anchor, calls)
+        cpu = cpu_baseline(wl, window, anchor, calls, sw)
     u_batched = unique_kv_bytes(wl, window, anchor, rows, wl.lens)
 
     res = {
@@ -576,6 +613,7 @@ def main():
                    "batch": wl.batch, "lens": wl.lens if wl.batch <= 8 else "ragged",
                    "mode": args.mode, "calls_per_layer": len(calls),
                    **({"draft_loops": min(args.draft_loops, wl.n_loops)} if args.mode == "draft" else {}),
+                   **({"draft_window": sw[1], "sinks": sw[0]} if sw is not None else {}),
                    "rows_per_call": len(rows) // len(calls),
                    "anchor": "query" if anchor == 0 else "cache",
                    "cache_copies": copies, "timing": "eager" if args.eager else "hip-graph"},

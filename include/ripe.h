@@ -189,6 +189,27 @@ ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
                              int32_t n_blk, float* d_out, float* d_lse, void* d_ws,
                              size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Windowed draft attention of one layer (page "Windowed-MTP: Removing the
+ * Full-Context Draft-KV Tax at Million-Token Context", abstract: a sliding
+ * window plus an attention sink on the draft's attention only, so a draft
+ * reads a bounded set of keys however long the context).  Arguments as for
+ * ripe_verify_attn, except that a row (i, r) of sequence b keeps only the
+ * committed positions s < n_sink (the sinks) and s >= L_b + i - w_draft (the
+ * window) among its keys; its draft-block keys 0..i all stay, and every key
+ * is read at the plane the verification rule names (with w_draft <= W the
+ * window's positions come from the ring at loop r, the sinks from the deepest
+ * plane).  n_sink >= 0 and w_draft >= 0, else RIPE_EINVAL; w_draft >= L + i
+ * is the full-context draft.  Needs no workspace; one workgroup reads a KV
+ * head's sinks and window, so it is meant for windows of up to a few
+ * thousand positions.
+ */
+ripe_status ripe_draft_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
+                            const int32_t* h_row_blk, const int32_t* h_row_loop,
+                            const void* d_q, ripe_kv_view blk_k, ripe_kv_view blk_v,
+                            int32_t n_blk, int32_t n_sink, int32_t w_draft, float* d_out,
+                            float* d_lse, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* ripe_status_string(ripe_status s);
 

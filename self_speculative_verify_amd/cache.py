@@ -92,3 +92,20 @@ class RipeCache:
                             _r.kv_view(blk_k, "bphtd"), _r.kv_view(blk_v, "bphtd"), n_blk,
                             out, lse, ws, stream)
         return out, lse
+
+    def draft(self, layer: int, rows: Sequence[Tuple[int, int]], q: torch.Tensor,
+              blk_k: torch.Tensor, blk_v: torch.Tensor, n_blk: int, n_sink: int, w_draft: int,
+              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Windowed draft attention: committed keys are the first n_sink
+        positions and the w_draft positions before each query."""
+        B, Hq, d = self.cfg.batch, self.cfg.n_heads_q, self.cfg.head_dim
+        n = len(rows)
+        if out is None:
+            out = torch.empty((B, n, Hq, d), dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, n, Hq), dtype=torch.float32, device=q.device)
+        _r.ripe_draft_attn(self.handle, layer, [i for i, _ in rows], [r for _, r in rows], q,
+                           _r.kv_view(blk_k, "bphtd"), _r.kv_view(blk_v, "bphtd"), n_blk,
+                           n_sink, w_draft, out, lse, stream)
+        return out, lse

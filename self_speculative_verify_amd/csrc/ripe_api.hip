@@ -125,7 +125,10 @@ int64_t extra_tiles(const Geometry& g, const uint32_t* rows, int rows_here, int 
     return most;
 }
 
-Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint32_t* rows) {
+// draft: a windowed draft call (the keys kernel, one chunk: it reads only the
+// sinks and a short window, and needs no workspace)
+Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint32_t* rows,
+               bool draft = false) {
     // tuning and test overrides: workgroup target, row tiles, kernel (1 keys, 2 rows)
     const int target_env = env_int("RIPE_ITEMS_TARGET", 0);
     const int force_rt = env_int("RIPE_ROW_TILES", 0);
@@ -134,7 +137,7 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
     Plan p;
     p.M = rows_here * (g.Hq / g.Hkv);
     // the rows kernel pays off once a KV head carries a hundred row-heads or more
-    p.rows_kernel = force_kernel ? force_kernel == 2 : p.M >= 128;
+    p.rows_kernel = draft ? false : force_kernel ? force_kernel == 2 : p.M >= 128;
     const int64_t heads = (int64_t)g.B * g.Hkv;
     int rows_per_item;
     if (p.rows_kernel) {
@@ -145,7 +148,7 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
         p.rt = std::min(p.M <= 16 ? 1 : 2, ripe::keys_max_row_tiles(g.d));
         rows_per_item = 16;
     }
-    if (force_rt > 0) p.rt = std::min(force_rt, p.rows_kernel ? ripe::rows_max_row_tiles(g.d)
+    if (force_rt > 0 && !draft) p.rt = std::min(force_rt, p.rows_kernel ? ripe::rows_max_row_tiles(g.d)
                                                               : ripe::keys_max_row_tiles(g.d));
     rows_per_item *= p.rt;
     p.nrb = (p.M + rows_per_item - 1) / rows_per_item;
@@ -154,7 +157,7 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
     // workgroups of one (sequence, chunk) pair, and of the whole call unsplit
     const int64_t units = (int64_t)g.Hkv * p.nrb;
     const int64_t base = g.B * units;
-    const int64_t slots = target_env ? target_env : (p.rows_kernel ? 256 : 512);
+    const int64_t slots = draft ? 0 : target_env ? target_env : (p.rows_kernel ? 256 : 512);
     const int64_t cx = 32 * extra_tiles(g, rows, rows_here, p.M, p.nrb, rows_per_item, lmax);
     const int64_t min_chunk = force_min_chunk ? force_min_chunk : std::max<int64_t>(256, 8 * rows_per_item);
     // One chunk length for every sequence, from their total: the pairs that
@@ -341,11 +344,16 @@ size_t ripe_workspace_bytes(const ripe_cache* cache, int32_t n_rows) {
     return ws;
 }
 
-ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
-                             const int32_t* h_row_blk, const int32_t* h_row_loop,
-                             const void* d_q, ripe_kv_view blk_k, ripe_kv_view blk_v,
-                             int32_t n_blk, float* d_out, float* d_lse, void* d_ws,
-                             size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// ripe_verify_attn (n_sink = 0, w_draft = -1) and ripe_draft_attn
+ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32_t* h_row_blk,
+                   const int32_t* h_row_loop, const void* d_q, ripe_kv_view blk_k,
+                   ripe_kv_view blk_v, int32_t n_blk, int32_t n_sink, int32_t w_draft,
+                   float* d_out, float* d_lse, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    const bool draft = w_draft >= 0;
     if (!live(cache) || layer < 0 || layer >= cache->g.n_layers) return RIPE_EINVAL;
     const Geometry& g = cache->g;
     if (n_rows < 0 || n_rows > 65535) return RIPE_EINVAL;
@@ -358,7 +366,7 @@ ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
         if (h_row_blk[k] < 0 || h_row_blk[k] >= n_blk) return RIPE_EINVAL;
         if (h_row_loop[k] < 1 || h_row_loop[k] > g.R) return RIPE_EINVAL;
     }
-    const size_t need = ripe_workspace_bytes(cache, n_rows);
+    const size_t need = draft ? 0 : ripe_workspace_bytes(cache, n_rows);
     if (ws_bytes < need || (need > 0 && (!d_ws || !aligned(d_ws, 256)))) return RIPE_EINVAL;
 
     // rows sorted by (loop, block offset) so that rows reading the same planes
@@ -387,11 +395,13 @@ ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
     a.R = g.R; a.d = g.d; a.n_blk = n_blk; a.anchor = g.anchor;
     a.W = g.W; a.CP = g.CP; a.WR = g.WR; a.WP = g.WP; a.NR = g.NR;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
+    a.n_sink = n_sink;
+    a.w_draft = w_draft;
     const int32_t* lens = cache->lens.data() + (size_t)layer * g.B;
     for (int k0 = 0; k0 < n_rows; k0 += ripe::kMaxRowsPerLaunch) {
         a.rows_here = std::min(ripe::kMaxRowsPerLaunch, n_rows - k0);
         for (int k = 0; k < a.rows_here; ++k) a.rows[k] = rows[k0 + k];
-        const Plan p = make_plan(g, lens, a.rows_here, a.rows);
+        const Plan p = make_plan(g, lens, a.rows_here, a.rows, draft);
         a.M = p.M; a.nrb = p.nrb; a.nc = p.nc; a.cl = p.cl; a.cx = p.cx; a.n_groups = p.n_groups;
         const hipError_t e = p.rows_kernel ? ripe::launch_verify_rows(a, p.rt, stream)
                                            : ripe::launch_verify_keys(a, p.rt, stream);
@@ -399,6 +409,29 @@ ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
         if (p.nc > 1 && ripe::launch_combine(a, stream) != hipSuccess) return RIPE_EDEVICE;
     }
     return RIPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
+                             const int32_t* h_row_blk, const int32_t* h_row_loop,
+                             const void* d_q, ripe_kv_view blk_k, ripe_kv_view blk_v,
+                             int32_t n_blk, float* d_out, float* d_lse, void* d_ws,
+                             size_t ws_bytes, hipStream_t stream) {
+    return attend(cache, layer, n_rows, h_row_blk, h_row_loop, d_q, blk_k, blk_v, n_blk, 0, -1,
+                  d_out, d_lse, d_ws, ws_bytes, stream);
+}
+
+ripe_status ripe_draft_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
+                            const int32_t* h_row_blk, const int32_t* h_row_loop,
+                            const void* d_q, ripe_kv_view blk_k, ripe_kv_view blk_v,
+                            int32_t n_blk, int32_t n_sink, int32_t w_draft, float* d_out,
+                            float* d_lse, hipStream_t stream) {
+    if (n_sink < 0 || w_draft < 0) return RIPE_EINVAL;
+    return attend(cache, layer, n_rows, h_row_blk, h_row_loop, d_q, blk_k, blk_v, n_blk, n_sink,
+                  w_draft, d_out, d_lse, nullptr, 0, stream);
 }
 
 const char* ripe_status_string(ripe_status s) {

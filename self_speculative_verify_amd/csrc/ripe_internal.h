@@ -89,6 +89,9 @@ struct VerifyArgs {
     int64_t cl;              // positions per chunk
     int64_t cx;              // positions' worth of ring and block tiles that the
                              // last chunk of a sequence carries besides its own
+    // windowed draft attention: a row (i, r) keeps the committed keys
+    // s < n_sink or s >= L + i - w_draft; w_draft < 0: every committed key
+    int32_t n_sink, w_draft;
     int32_t n_groups;        // B * Hkv * nc
     // rows of this launch sorted by (loop, block offset):
     // bits 0..7 block offset, 8..15 loop, 16..31 row index in the call

@@ -71,6 +71,7 @@ struct RowTile {
     f32x4 o[D / 16];      // O^T: dims 16dt + 4q..+4 of row-head n
     int ri;               // bits 0..7 block offset, 8..15 loop, bit 16 valid
     int e;                // loop-R positions of this row-head end here (e_row)
+    int lo;               // windowed draft: committed keys from here on (and sinks)
 };
 #define RI_OK(x) (((x) >> 16) & 1)
 #define RI_R(x) (((x) >> 8) & 255)
@@ -359,6 +360,7 @@ __device__ inline void init_row_word(const VerifyArgs& a, const Item& it, int u,
     const int ii = rw & 255, rr = (rw >> 8) & 255;
     rt.ri = ii | (rr << 8) | (ok ? 1 << 16 : 0);
     rt.e = e_row(a, it.L, ii, rr);
+    rt.lo = a.w_draft < 0 ? 0 : max(0, it.L + ii - a.w_draft);
     rt.m = -INFINITY;
     rt.l = 0.f;
 #pragma unroll
@@ -394,6 +396,22 @@ __device__ inline int mask_ring(const RowTile<D>& rt, const Item& it, int WR, in
         v[e] = mine && sl < it.nsl && pos >= rt.e;
     }
     return 1;
+}
+// windowed draft: of a deep (kind 0) or ring (kind 1) tile's keys that the
+// masks above let through (mode 1: v; mode 2: all of them), keep the sinks
+// s < n_sink and the window s >= lo
+template <int D>
+__device__ inline int mask_window(const RowTile<D>& rt, const Item& it, int kind, int base, int n_sink,
+                                  int WR, int q, int mode, bool (&v)[8]) {
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        int s = base + key_of(e, q);
+        if (kind == 1) s = it.ring_base + s - (s > it.ring_top ? WR : 0);   // ring slot -> position
+        v[e] = (mode == 2 ? (bool)RI_OK(rt.ri) : v[e]) && (s < n_sink || s >= rt.lo);
+        any = any || v[e];
+    }
+    return __any(any) ? 1 : 0;
 }
 template <int D>
 __device__ inline int mask_block(const RowTile<D>& rt, int r, int base, int q, bool (&v)[8]) {
@@ -1055,7 +1073,8 @@ struct Job {
     const uint16_t* V;
 };
 
-template <int D, int RT>
+// WIN: windowed draft attention (sinks and a window of committed keys)
+template <int D, int RT, bool WIN>
 __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
     constexpr int kStage = 4 * 2 * 32 * D;             // uint16: per-wave block tiles
     constexpr int kMerge = 2 * RT * 16 * (D + 2);      // floats: merge buffers
@@ -1119,7 +1138,21 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
     const int n_ring_planes = nloops - (has_R ? 1 : 0);
 
     const int d1 = (int)min((int64_t)d0 + a.cl, (int64_t)E);
-    const int n_deep = d1 > d0 ? (d1 - d0 + 31) / 32 : 0;
+    const int n_deep_all = d1 > d0 ? (d1 - d0 + 31) / 32 : 0;
+    // a windowed draft skips the deep tiles that lie wholly between the sinks
+    // and the lowest window start of the workgroup's rows: tiles gap_at ..
+    // gap_at + gap_n - 1 of the chunk
+    constexpr bool windowed = WIN;
+    int gap_at = n_deep_all, gap_n = 0;
+    if (windowed) {
+        const int lo_min = wave_min(lane < nk ? max(0, it.L + ii - a.w_draft) : 0x7fffffff);
+        const int g0 = max(d0, (a.n_sink + 31) / 32 * 32), g1 = min(d1, lo_min / 32 * 32);
+        if (g1 > g0) {
+            gap_at = (g0 - d0) / 32;
+            gap_n = (g1 - g0) / 32;
+        }
+    }
+    const int n_deep = n_deep_all - gap_n;
     const int ring_tiles = (it.last && a.R > 1 && it.nsl > 0) ? (it.nsl + 31) / 32 : 0;
     const int n_ring = n_ring_planes * ring_tiles;
     const int n_block = it.last ? __builtin_amdgcn_readlane(bend, 63) : 0;
@@ -1134,7 +1167,7 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
         if (j < n_deep) {
             jb.kind = 0;
             jb.r = a.R;
-            jb.base = d0 + j * 32;
+            jb.base = d0 + (j < gap_at ? j : j + gap_n) * 32;
             jb.K = a.deep_k + dreg + (int64_t)jb.base * D;
             jb.V = a.deep_v + dreg + (int64_t)jb.base * D;
             return jb;
@@ -1166,7 +1199,7 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
     // computes the current one.  Those loads are unconditional (past its last
     // committed tile a wave reloads the first deep tile and ignores it), so
     // the compiler counts them exactly.
-    constexpr bool kAhead = D * RT <= 128;
+    constexpr bool kAhead = WIN ? D * RT < 128 : D * RT <= 128;
     const int n_comm = n_deep + n_ring;
     auto comm_load = [&](int j, Frags<D>& f) {
         const uint16_t* K = a.deep_k + dreg;
@@ -1178,7 +1211,7 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
         }
         load_frags<D>(K, V, f, n, q);
     };
-    if (wave >= n_deep) comm_load(wave, f);
+    if (wave >= n_deep || wave >= gap_at) comm_load(wave, f);   // not the tile requested early
     RowTile<D> rt[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
@@ -1206,6 +1239,8 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
             if (kind == 0) mode = mask_deep<D>(rt[tr], base, d1, q, v);
             else if (kind == 1) mode = mask_ring<D>(rt[tr], it, (int)a.WR, jr, base, q, v);
             else mode = mask_block<D>(rt[tr], jr, base, q, v);
+            if (windowed && kind < 2 && mode)
+                mode = mask_window<D>(rt[tr], it, kind, base, a.n_sink, (int)a.WR, q, mode, v);
             if (mode) tile_update<D>(rt[tr], f, mode == 2, v, sl2);
         }
         if (kAhead) f = fn;
@@ -1343,12 +1378,18 @@ int rows_max_row_tiles(int d) { return d == 96 ? 1 : 2; }
 
 hipError_t launch_verify_keys(const VerifyArgs& a, int rt, hipStream_t s) {
     if (rt < 1 || rt > keys_max_row_tiles(a.d)) return hipErrorInvalidValue;
-    switch (a.d * 4 + rt) {
-        case 64 * 4 + 1: return launch_items(k_verify_keys<64, 1>, a, s);
-        case 64 * 4 + 2: return launch_items(k_verify_keys<64, 2>, a, s);
-        case 96 * 4 + 1: return launch_items(k_verify_keys<96, 1>, a, s);
-        case 96 * 4 + 2: return launch_items(k_verify_keys<96, 2>, a, s);
-        case 128 * 4 + 1: return launch_items(k_verify_keys<128, 1>, a, s);
+    const bool win = a.w_draft >= 0;
+    switch (a.d * 8 + rt * 2 + (win ? 1 : 0)) {
+        case 64 * 8 + 2: return launch_items(k_verify_keys<64, 1, false>, a, s);
+        case 64 * 8 + 4: return launch_items(k_verify_keys<64, 2, false>, a, s);
+        case 96 * 8 + 2: return launch_items(k_verify_keys<96, 1, false>, a, s);
+        case 96 * 8 + 4: return launch_items(k_verify_keys<96, 2, false>, a, s);
+        case 128 * 8 + 2: return launch_items(k_verify_keys<128, 1, false>, a, s);
+        case 64 * 8 + 3: return launch_items(k_verify_keys<64, 1, true>, a, s);
+        case 64 * 8 + 5: return launch_items(k_verify_keys<64, 2, true>, a, s);
+        case 96 * 8 + 3: return launch_items(k_verify_keys<96, 1, true>, a, s);
+        case 96 * 8 + 5: return launch_items(k_verify_keys<96, 2, true>, a, s);
+        case 128 * 8 + 3: return launch_items(k_verify_keys<128, 1, true>, a, s);
     }
     return hipErrorInvalidValue;
 }

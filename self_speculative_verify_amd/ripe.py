@@ -20,6 +20,7 @@ __all__ = [
     "RipeConfig", "RipeKVView", "RipeError", "library_path", "load",
     "ripe_cache_bytes", "ripe_section_offset", "ripe_max_batch", "ripe_cache_create", "ripe_destroy",
     "ripe_get_lengths", "ripe_append", "ripe_workspace_bytes", "ripe_verify_attn",
+    "ripe_draft_attn",
     "ripe_status_string", "kv_view", "null_view", "config",
 ]
 
@@ -83,6 +84,9 @@ def load():
         L.ripe_verify_attn.restype = I32
         L.ripe_verify_attn.argtypes = [P, I32, I32, P, P, P, RipeKVView, RipeKVView, I32,
                                        P, P, P, SZ, P]
+        L.ripe_draft_attn.restype = I32
+        L.ripe_draft_attn.argtypes = [P, I32, I32, P, P, P, RipeKVView, RipeKVView, I32, I32, I32,
+                                      P, P, P]
         L.ripe_status_string.restype = ctypes.c_char_p
         L.ripe_status_string.argtypes = [I32]
         _LIB = L
@@ -194,3 +198,20 @@ def ripe_verify_attn(handle, layer: int, row_blk: Sequence[int], row_loop: Seque
                                    blk_k, blk_v, n_blk, ctypes.c_void_p(out.data_ptr()),
                                    ctypes.c_void_p(lse.data_ptr()), ws_ptr, ws_bytes,
                                    _stream(stream)), "ripe_verify_attn")
+
+
+def ripe_draft_attn(handle, layer: int, row_blk: Sequence[int], row_loop: Sequence[int],
+                    q: torch.Tensor, blk_k: RipeKVView, blk_v: RipeKVView, n_blk: int,
+                    n_sink: int, w_draft: int, out: torch.Tensor, lse: torch.Tensor,
+                    stream=None) -> None:
+    if len(row_blk) != len(row_loop):
+        raise ValueError("row_blk and row_loop differ in length")
+    for t, name, dt in ((q, "q", torch.bfloat16), (out, "out", torch.float32),
+                        (lse, "lse", torch.float32)):
+        if not t.is_cuda or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    _check(load().ripe_draft_attn(handle, layer, len(row_blk), _i32_array(row_blk),
+                                  _i32_array(row_loop), ctypes.c_void_p(q.data_ptr()),
+                                  blk_k, blk_v, n_blk, int(n_sink), int(w_draft),
+                                  ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
+                                  _stream(stream)), "ripe_draft_attn")

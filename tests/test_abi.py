@@ -69,6 +69,7 @@ def test_null_handles_and_pointers_rejected():
     assert L.ripe_append(None, 0, n, v, v, v, v, None) == ripe.RIPE_EINVAL
     assert L.ripe_verify_attn(None, 0, 1, n, n, None, v, v, 1, None, None, None, 0, None) == ripe.RIPE_EINVAL
     assert L.ripe_workspace_bytes(None, 4) == 0
+    assert L.ripe_draft_attn(None, 0, 1, n, n, None, v, v, 1, 0, 4, None, None, None) == ripe.RIPE_EINVAL
     L.ripe_destroy(None)
     c = ripe.config(1, 4, 2, 2, 64, 8, 1, 64, 4)
     h = ctypes.c_void_p()
