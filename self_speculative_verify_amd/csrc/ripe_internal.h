@@ -98,7 +98,6 @@ struct VerifyArgs {
     uint32_t rows[kMaxRowsPerLaunch];
 };
 
-hipError_t launch_verify_valu(const VerifyArgs& a, hipStream_t s);
 // matrix-core kernels: "keys" (waves split the key tiles of 16*rt row-heads)
 // and "rows" (each wave owns 16*rt row-heads; the workgroup 64*rt)
 int keys_max_row_tiles(int d);
