@@ -35,8 +35,10 @@
  * synchronisation.  A handle is not thread-safe; calls that use one storage
  * from several streams must be ordered by the caller.
  *
- * Errors.  Every argument is checked before anything is enqueued; a call that
- * returns an error has enqueued nothing and changed no state.
+ * Errors.  Every argument is checked before anything is enqueued: a call
+ * that returns RIPE_EINVAL or RIPE_ECAPACITY has enqueued nothing and changed
+ * no state.  RIPE_EDEVICE means a launch failed part-way; the storage and the
+ * lengths are then undefined.
  */
 #ifndef RIPE_H
 #define RIPE_H

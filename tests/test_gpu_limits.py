@@ -1,0 +1,81 @@
+"""GPU parity at the edges of the launch configuration: calls with more rows
+than one launch takes (256), batches larger than one append launch takes (64),
+draft blocks longer than one 32-key tile, and windows longer than the
+capacity.  Same bar as the other parity tests (bit-exact layout, max |dO| <=
+2e-3, relative LSE error <= 1e-5), against the fp64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import WINDOW_FULL, Workload, grid_rows, ragged_lengths
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 2e-3
+TOL_LSE = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import self_speculative_verify_amd.ripe as r
+    r.load()
+    yield
+
+
+@pytest.fixture(params=["auto", "keys", "rows", "keys-chunked"], autouse=True)
+def kernel_choice(request, monkeypatch):
+    if request.param in ("keys", "keys-chunked"):
+        monkeypatch.setenv("RIPE_KERNEL", "1")
+    if request.param == "rows":
+        monkeypatch.setenv("RIPE_KERNEL", "2")
+    if request.param == "keys-chunked":
+        monkeypatch.setenv("RIPE_ITEMS_TARGET", "100000")
+        monkeypatch.setenv("RIPE_MIN_CHUNK", "32")
+    yield request.param
+
+
+def run(wl, rows=None):
+    import ripe_harness as H
+    cache = H.make_cache(wl)
+    H.load_prefix(cache, wl)
+    oc = oracle.prefix_cache(wl, layers=[0])
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.storage.cpu().numpy(), oc.image), "layout differs from the oracle"
+    rows = wl.rows if rows is None else rows
+    q, bk, bv = H.verify_inputs(wl, 0)
+    out, lse = cache.verify(0, rows, q, bk, bv, wl.n_blk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oc.verify(0, rows, wl.queries(0), *wl.block(0), wl.n_blk)
+    o = out.cpu().double().numpy()
+    l = lse.cpu().double().numpy()
+    err_o = float(np.max(np.abs(o - ref_o)))
+    err_l = float(np.max(np.abs(l - ref_l) / np.maximum(1.0, np.abs(ref_l))))
+    print(f"{wl.name}: {len(rows)} rows, batch {wl.batch}: max|dO|={err_o:.3e} rel dLSE={err_l:.3e}",
+          flush=True)
+    assert err_o <= TOL_O and err_l <= TOL_LSE
+
+
+def test_more_rows_than_one_launch():
+    """12 x 24 = 288 rows: two launches of one call."""
+    run(Workload("rows288", 91, 1, 24, 4, 2, 64, 16, 12, [150, 61], 0.88, grid_rows(12, 24),
+                 heavy_frac=0.05))
+
+
+def test_batch_larger_than_one_append_launch():
+    """70 sequences of ragged lengths (two append launches per layer)."""
+    lens = ragged_lengths(92, 70, 0, 90)
+    run(Workload("b70", 92, 1, 4, 2, 1, 64, 12, 3, lens, 0.88, grid_rows(3, 4)))
+
+
+@pytest.mark.parametrize("D", [33, 40])
+def test_draft_block_longer_than_a_tile(D):
+    run(Workload(f"blk{D}", 93, 1, 3, 4, 4, 96, 48, D, [200, 7], 0.88, grid_rows(D, 3)))
+
+
+@pytest.mark.parametrize("W", [500, WINDOW_FULL])
+def test_window_longer_than_the_capacity(W):
+    run(Workload("wcap", 94, 1, 6, 4, 2, 128, W, 4, [120, 300, 33], 0.81, grid_rows(4, 6)))
