@@ -87,6 +87,7 @@ bool view_ok(const ripe_kv_view& v) {
 // its row block, so it reads cx fewer committed positions than the others.
 struct Plan {
     bool rows_kernel;
+    bool priv;         // rows kernel with private waves for the ring and block tiles
     int rt, nrb, nc, n_groups, M;
     int64_t cl, cx;
     size_t ws_bytes;
@@ -134,6 +135,7 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
     const int force_rt = env_int("RIPE_ROW_TILES", 0);
     const int force_kernel = env_int("RIPE_KERNEL", 0);
     const int force_min_chunk = env_int("RIPE_MIN_CHUNK", 0);
+    const int force_priv = env_int("RIPE_PRIV", 0);      // 1 off, 2 on
     Plan p;
     p.M = rows_here * (g.Hq / g.Hkv);
     // the rows kernel pays off once a KV head carries a hundred row-heads or more
@@ -151,6 +153,9 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
     if (force_rt > 0 && !draft) p.rt = std::min(force_rt, p.rows_kernel ? ripe::rows_max_row_tiles(g.d)
                                                               : ripe::keys_max_row_tiles(g.d));
     rows_per_item *= p.rt;
+    // private waves pay off when the row blocks have ring tiles to read
+    p.priv = p.rows_kernel && ripe::rows_private_waves(g.d, p.rt) &&
+             (force_priv ? force_priv == 2 : (g.R > 1 && g.WR > 0));
     p.nrb = (p.M + rows_per_item - 1) / rows_per_item;
     int64_t lmax = 0;
     for (int b = 0; b < g.B; ++b) lmax = std::max<int64_t>(lmax, lens[b]);
@@ -403,7 +408,7 @@ ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32
         for (int k = 0; k < a.rows_here; ++k) a.rows[k] = rows[k0 + k];
         const Plan p = make_plan(g, lens, a.rows_here, a.rows, draft);
         a.M = p.M; a.nrb = p.nrb; a.nc = p.nc; a.cl = p.cl; a.cx = p.cx; a.n_groups = p.n_groups;
-        const hipError_t e = p.rows_kernel ? ripe::launch_verify_rows(a, p.rt, stream)
+        const hipError_t e = p.rows_kernel ? ripe::launch_verify_rows(a, p.rt, p.priv, stream)
                                            : ripe::launch_verify_keys(a, p.rt, stream);
         if (e != hipSuccess) return RIPE_EDEVICE;
         if (p.nc > 1 && ripe::launch_combine(a, stream) != hipSuccess) return RIPE_EDEVICE;

@@ -103,7 +103,9 @@ struct VerifyArgs {
 int keys_max_row_tiles(int d);
 int rows_max_row_tiles(int d);
 hipError_t launch_verify_keys(const VerifyArgs& a, int rt, hipStream_t s);
-hipError_t launch_verify_rows(const VerifyArgs& a, int rt, hipStream_t s);
+// priv: four more waves take the ring and draft-block tiles (where rows_private_waves)
+bool rows_private_waves(int d, int rt);
+hipError_t launch_verify_rows(const VerifyArgs& a, int rt, bool priv, hipStream_t s);
 hipError_t launch_combine(const VerifyArgs& a, hipStream_t s);
 
 }  // namespace ripe

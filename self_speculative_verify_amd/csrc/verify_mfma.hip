@@ -595,6 +595,211 @@ __device__ inline void lds_values(const uint16_t* stage, Frags<D>& f, int lane) 
     for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = p[(D / 16 + dt) * 64];
 }
 
+// The private wave of row group rw in the rows kernel (PRIV): the ring tiles
+// of the row group's loops while the deep tiles stream (one tile every second
+// step, loaded two steps ahead into registers, so its loads never hold back
+// a barrier), then its draft-block tiles, staged in a wave-private part of
+// the stages once they are free; its state goes to the second merge buffer.
+// It executes exactly the barriers of the other waves: one before the loop,
+// n_iter in it, four after it.
+template <int D, int RTW>
+__device__ __attribute__((always_inline)) inline void private_wave(const VerifyArgs& a, const Item& it,
+        RowTile<D> (&rt)[RTW], int rw, int u_w, int n_iter, int ring_tiles, int64_t rreg0,
+        int64_t WPD, float sl2, int lane, uint16_t* stages, const uint4* sq, int merge_slots) {
+    constexpr int TILE = 32 * D;
+    constexpr int MS = D / 4 + 2;
+    const int n = lane & 15, q = lane >> 4;
+    asm volatile("s_barrier ; private: queries and tile 0" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < RTW; ++t)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) rt[t].q[c] = sq[(t * (D / 32) + c) * 64 + lane];
+    // the row group's row-heads x = 16t + n in lanes x (x < 16*RTW), sorted by
+    // loop then block offset: the first of each loop marks it, the last one
+    // carries the loop's largest offset
+    // (the shuffle runs in every lane: a lane that is switched off cannot be a source)
+    const int ri_hi = __shfl(rt[RTW - 1].ri, (lane + 48) & 63);
+    const int ri = lane < 16 ? rt[0].ri : (RTW == 2 && lane < 32 ? ri_hi : 0);
+    const int ri_prev = __shfl(ri, (lane + 63) & 63), ri_next = __shfl(ri, (lane + 1) & 63);
+    const bool ok = RI_OK(ri), ok_p = lane > 0 && RI_OK(ri_prev), ok_n = lane < 63 && RI_OK(ri_next);
+    const bool first = ok && (!ok_p || RI_R(ri_prev) != RI_R(ri));
+    const bool last = ok && (!ok_n || RI_R(ri_next) != RI_R(ri));
+    const uint64_t fmask = __ballot(first), lmask = __ballot(last);
+    (void)u_w;
+    // ring jobs: (loop p with r < R, slot tile st), p-major
+    int n_ring_loops = 0;
+    {
+        uint64_t m = fmask;
+        while (m) {
+            const int k = __builtin_ctzll(m);
+            m &= m - 1;
+            n_ring_loops += (int)RI_R(__builtin_amdgcn_readlane(ri, k)) < a.R;
+        }
+    }
+    const int n_jobs = it.last ? n_ring_loops * ring_tiles : 0;
+    // job j -> ring tile address and loop (wave-uniform)
+    auto job = [&](int j, int& r, int& base) -> int64_t {
+        const int pl = j / ring_tiles, st = j % ring_tiles;
+        uint64_t m = fmask;
+        int seen = -1, rr = a.R;
+        while (m) {
+            const int k = __builtin_ctzll(m);
+            m &= m - 1;
+            rr = (int)RI_R(__builtin_amdgcn_readlane(ri, k));
+            if (rr < a.R && ++seen == pl) break;
+        }
+        r = rr;
+        base = st * 32;
+        return rreg0 + (int64_t)(rr - 1) * WPD + (int64_t)st * TILE;
+    };
+    // One register buffer: a job is loaded, then computed two barriers later
+    // (odd steps), and only then is the next one loaded into the same
+    // registers; the loads stay in flight across barriers, which do not wait
+    // for them.  Jobs left after the loop run one after the other.
+    Frags<D> fr;
+    int rr = 0, br = 0;
+    auto load_job = [&](int j) {
+        const int64_t off = job(j, rr, br);
+        load_frags<D>(a.ring_k + off, a.ring_v + off, fr, n, q);
+    };
+    auto run_job = [&]() {
+#pragma unroll
+        for (int tr = 0; tr < RTW; ++tr) {
+            bool v[8];
+            if (mask_ring<D>(rt[tr], it, (int)a.WR, rr, br, q, v)) tile_update<D>(rt[tr], fr, false, v, sl2);
+        }
+    };
+    // Draft-block rows: in the common case (at most two loops in the row
+    // group, offsets below 8) they are requested into registers now, as
+    // pieces pc = (kv*8 + key)*(D/8) + c8 with lane holding pc = lane + 64k,
+    // and staged only after the loop; other row sets load them then.
+    constexpr int PB = D / 32;
+    const int nloops = __popcll(fmask);
+    int blk_r[2] = {0, 0}, blk_im[2] = {-1, -1};
+    {
+        uint64_t m = fmask;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            if (m) {
+                const int k = __builtin_ctzll(m);
+                m &= m - 1;
+                blk_r[p] = (int)RI_R(__builtin_amdgcn_readlane(ri, k));
+                blk_im[p] = (int)RI_I(__builtin_amdgcn_readlane(ri, __builtin_ctzll(lmask & (~0ull << k))));
+            }
+        }
+    }
+    // (not with two row tiles of 64 dims, whose registers are needed)
+    constexpr bool kBlkPf = D * RTW <= 96;
+    const bool pf_ok = kBlkPf && it.last && nloops <= 2 && blk_im[0] < 8 && blk_im[1] < 8;
+    uint4 pfb[2][PB];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const uint16_t* pbk = a.bk.p + it.b * a.bk.sb + (int64_t)(max(blk_r[p], 1) - 1) * a.bk.sp + it.g * a.bk.sh;
+        const uint16_t* pbv = a.bv.p + it.b * a.bv.sb + (int64_t)(max(blk_r[p], 1) - 1) * a.bv.sp + it.g * a.bv.sh;
+#pragma unroll
+        for (int k = 0; k < PB; ++k) {
+            const int pc = lane + 64 * k;
+            const int c8 = pc % (D / 8), rest = pc / (D / 8);
+            const int key = rest % 8, kv = rest / 8;
+            pfb[p][k] = make_uint4(0, 0, 0, 0);
+            if (pf_ok && p < nloops && key < a.n_blk && key <= blk_im[p])
+                pfb[p][k] = *reinterpret_cast<const uint4*>((kv ? pbv + key * a.bv.st : pbk + key * a.bk.st) + c8 * 8);
+        }
+    }
+    int done = 0;
+    if (n_jobs > 0) load_job(0);
+    for (int k = 0; k < n_iter; ++k) {
+        asm volatile("s_barrier" ::: "memory");
+        if ((k & 1) == 1 && done < n_jobs) {
+            run_job();
+            if (++done < n_jobs) load_job(done);
+        }
+    }
+    while (done < n_jobs) {
+        run_job();
+        if (++done < n_jobs) load_job(done);
+    }
+    // every deep load is done and every wave has left the stages
+    lds_barrier();
+    if (it.last && pf_ok) {
+        uint16_t* sk = stages + rw * 2 * TILE;
+        uint16_t* sv = sk + TILE;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            if (p >= nloops) break;
+            for (int z = lane; z < 2 * TILE / 8; z += 64)
+                *reinterpret_cast<uint4*>(sk + z * 8) = make_uint4(0, 0, 0, 0);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int k = 0; k < PB; ++k) {
+                const int pc = lane + 64 * k;
+                const int c8 = pc % (D / 8), rest = pc / (D / 8);
+                const int key = rest % 8, kv = rest / 8;
+                if (kv == 0) {
+                    *reinterpret_cast<uint4*>(sk + key_off(key, c8 * 8, D)) = pfb[p][k];
+                } else {
+                    const uint32_t w[4] = {pfb[p][k].x, pfb[p][k].y, pfb[p][k].z, pfb[p][k].w};
+#pragma unroll
+                    for (int cc = 0; cc < 8; ++cc)
+                        sv[val_off(key, c8 * 8 + cc, D)] = (uint16_t)(w[cc >> 1] >> (16 * (cc & 1)));
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            Frags<D> f;
+            load_frags<D>(sk, sv, f, n, q);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int tr = 0; tr < RTW; ++tr) {
+                bool v[8];
+                if (mask_block<D>(rt[tr], blk_r[p], 0, q, v)) tile_update<D>(rt[tr], f, false, v, sl2);
+            }
+        }
+    } else if (it.last) {
+        uint16_t* sk = stages + rw * 2 * TILE;
+        uint16_t* sv = sk + TILE;
+        uint64_t m = fmask;
+        while (m) {
+            const int k = __builtin_ctzll(m);
+            m &= m - 1;
+            const int r = (int)RI_R(__builtin_amdgcn_readlane(ri, k));
+            // the loop's last row-head is the first marked last at or after k
+            const uint64_t after = lmask & (~0ull << k);
+            const int imax = (int)RI_I(__builtin_amdgcn_readlane(ri, __builtin_ctzll(after)));
+            const uint16_t* bK = a.bk.p + it.b * a.bk.sb + (int64_t)(r - 1) * a.bk.sp + it.g * a.bk.sh;
+            const uint16_t* bV = a.bv.p + it.b * a.bv.sb + (int64_t)(r - 1) * a.bv.sp + it.g * a.bv.sh;
+            for (int base = 0; base <= imax; base += 32) {
+                stage_block<D>(a, bK, bV, base, sk, sv, lane);
+                Frags<D> f;
+                load_frags<D>(sk, sv, f, n, q);
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int tr = 0; tr < RTW; ++tr) {
+                    bool v[8];
+                    if (mask_block<D>(rt[tr], r, base, q, v)) tile_update<D>(rt[tr], f, false, v, sl2);
+                }
+            }
+        }
+    }
+    lds_barrier();                                 // the merge buffers are free
+    // second merge buffer: after the first one's merge_slots lane states
+    float* s_m = reinterpret_cast<float*>(stages) + merge_slots * MS;
+#pragma unroll
+    for (int tr = 0; tr < RTW; ++tr) {
+        float* dst = s_m + ((rw * RTW + tr) * 64 + lane) * MS;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[dt * 4 + j] = rt[tr].o[dt][j];
+        dst[D / 4] = rt[tr].m;
+        dst[D / 4 + 1] = rt[tr].l;
+    }
+    lds_barrier();                                 // half 0 merges
+    lds_barrier();                                 // merge buffers free again
+}
+
 // Eight waves: waves w and w+4 own the same 16*RTW row-heads and take the
 // even and odd tiles of the stream (key halves kh = 0, 1), so every SIMD runs
 // two independent tile steps; their softmax states merge through LDS at the end.
@@ -606,8 +811,15 @@ __device__ inline void lds_values(const uint16_t* stage, Frags<D>& f, int lane) 
 // the merge, so the compiler never drains the load pipeline; all waits on the
 // direct loads are explicit.  Deep tiles that every row-head reads in full take
 // the unmasked step.
-template <int D, int RTW>
-__global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
+//
+// PRIV: four more waves, one per row group, take the ring and draft-block
+// tiles of their row group's loops, which no other row group reads, straight
+// from memory into registers, while the eight waves stream only the deep tiles
+// through LDS; the private waves join every barrier and their softmax state
+// joins the merge.  The ring phase then runs beside the deep phase instead of
+// after it.
+template <int D, int RTW, bool PRIV>
+__global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs a) {
     constexpr int TILE = 32 * D;                 // elements of one K or V tile
     // LDS pipeline stages (one tile pair per half each): 128 / 144 / 128 KB
     constexpr int S = D == 128 ? 4 : (D == 96 ? 6 : 8);
@@ -616,14 +828,14 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     constexpr int MS = D / 4 + 2;                // floats of one lane's state in the merge
     __shared__ __attribute__((aligned(16))) uint16_t s_tile[S][2][2 * TILE];
     __shared__ __attribute__((aligned(16))) uint4 s_q[4][RTW * (D / 32)][64];   // query operands per row group
-    static_assert(4 * RTW * 64 * MS * 4 <= (int)sizeof(s_tile), "merge buffer");
+    static_assert((PRIV ? 2 : 1) * 4 * RTW * 64 * MS * 4 <= (int)sizeof(s_tile), "merge buffers");
     static_assert(8 * 2 * TILE * 2 <= (int)sizeof(s_tile), "per-wave block scratch");
     static_assert(RTW <= 2, "two row words per lane");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, n = lane & 15, q = lane >> 4;
-    const int rw = wave & 3, kh = wave >> 2;     // row group, key half
+    const int rw = wave & 3, kh = wave >> 2;     // row group, key half (2: private wave)
     const int G = a.group;
     // the workgroup's rows k_lo .. k_lo+nk-1 (sorted by loop, then block
     // offset), loaded first since they do not depend on the sequence: row
@@ -713,7 +925,7 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     const int d1 = min(d0 + cl, E);
     const int n_deep = d1 > d0 ? (d1 - d0 + 31) / 32 : 0;
     const int ring_tiles = (it.last && a.R > 1 && it.nsl > 0) ? (it.nsl + 31) / 32 : 0;
-    const int n_tiles = n_deep + nl * ring_tiles;
+    const int n_tiles = n_deep + (PRIV ? 0 : nl * ring_tiles);
     const int n_iter = (n_tiles + 1) / 2;
     const int64_t rreg0 = ((int64_t)it.b * a.Hkv + it.g) * a.NR * a.WP * D;
     const int64_t WPD = a.WP * D;
@@ -732,13 +944,21 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     const int n_full = min(e_lb, d1) > d0 ? (min(e_lb, d1) - d0) / 32 : 0;
     const int n_fast = min(n_iter, n_full / 2);
 
+    if constexpr (PRIV) {
+        if (kh == 2) {
+            private_wave<D, RTW>(a, it, rt, rw, u_w, n_iter, ring_tiles, rreg0, WPD, sl2, lane,
+                                 &s_tile[0][0][0], &s_q[rw][0][0], 4 * RTW * 64);
+            return;
+        }
+    }
+
     // issue cursor: the j-th issue of this wave loads tile 2j + kh of the stream
     int ti = kh, ipl = 0, ist = 0;
     const uint16_t* iK = gK + (int64_t)(d0 + 32 * kh) * D;
     const uint16_t* iV = gV + (int64_t)(d0 + 32 * kh) * D;
     int issued = 0;                               // tile pairs issued by this wave
     auto issue_next = [&](uint16_t* stage) {
-        if (ti < n_deep) {
+        if (PRIV || ti < n_deep) {                // with private waves the stream is deep only
             load_stage_asm<D>(iK, iV, stage, rw, lane);
         } else {
             if (ti - 2 < n_deep) { ipl = 0; ist = ti - n_deep; }   // first ring tile of this half
@@ -807,7 +1027,7 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     // lane holds pc = lane + 64k.
     constexpr int PB = D / 32;                   // prefetched pieces per lane
     // (not with 256 dims of row tiles per wave, whose steps need those registers)
-    constexpr bool kPf = D * RTW < 256;
+    constexpr bool kPf = D * RTW < 256 && !PRIV;
     const bool pf_ok = kPf && it.last && !wl_more && kh < n_wl && (kh ? wimax[1] : wimax[0]) < 8;
     uint4 pf[PB];
     if (kPf) {
@@ -894,7 +1114,7 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
         int mode[RTW];                            // 0 skip, 1 masked, 2 full
         bool v[RTW][8];
         if (t < n_tiles) {
-            if (t < n_deep) {
+            if (PRIV || t < n_deep) {
                 const int base = d0 + 32 * t;
 #pragma unroll
                 for (int tr = 0; tr < RTW; ++tr) {
@@ -935,7 +1155,7 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     lds_barrier();
     // draft-block tiles of the wave's loop slot kh, staged in a wave-private
     // part of the stages (K in storage order, V transposed)
-    if (it.last && kh < n_wl) {
+    if (!PRIV && it.last && kh < n_wl) {
         uint16_t* sk = &s_tile[0][0][0] + (rw * 2 + kh) * 2 * TILE;
         uint16_t* sv = sk + TILE;
         const int r = kh ? wl[1] : wl[0];
@@ -998,23 +1218,26 @@ __global__ void __launch_bounds__(512, 1) k_verify_rows(VerifyArgs a) {
     if (kh == 0) {
 #pragma unroll
         for (int tr = 0; tr < RTW; ++tr) {
-            const float* src = s_m + ((rw * RTW + tr) * 64 + lane) * MS;
-            const float m2 = src[D / 4], l2 = src[D / 4 + 1];
-            const float mn = fmaxf(rt[tr].m, m2);
-            const float w1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((rt[tr].m - mn) * sl2);
-            const float w2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * sl2);
-            rt[tr].m = mn;
-            rt[tr].l = rt[tr].l * w1 + l2 * w2;
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
+            for (int src_i = 0; src_i < (PRIV ? 2 : 1); ++src_i) {
+                const float* src = s_m + (src_i * 4 * RTW * 64 + (rw * RTW + tr) * 64 + lane) * MS;
+                const float m2 = src[D / 4], l2 = src[D / 4 + 1];
+                const float mn = fmaxf(rt[tr].m, m2);
+                const float w1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((rt[tr].m - mn) * sl2);
+                const float w2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * sl2);
+                rt[tr].m = mn;
+                rt[tr].l = rt[tr].l * w1 + l2 * w2;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) rt[tr].o[dt][j] = rt[tr].o[dt][j] * w1 + src[dt * 4 + j] * w2;
+                for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) rt[tr].o[dt][j] = rt[tr].o[dt][j] * w1 + src[dt * 4 + j] * w2;
+            }
         }
     }
     lds_barrier();                                 // merge buffer free again
     if (kh == 1) return;
 
-    if (it.last) {
+    if (!PRIV && it.last) {
         uint16_t* sk = &s_tile[0][0][0] + rw * 2 * TILE;   // per-wave scratch in the stages
         uint16_t* sv = sk + TILE;
         if (wl_more) {
@@ -1394,14 +1617,23 @@ hipError_t launch_verify_keys(const VerifyArgs& a, int rt, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_verify_rows(const VerifyArgs& a, int rtw, hipStream_t s) {
+bool rows_private_waves(int d, int rtw) { return d * rtw < 256; }
+
+hipError_t launch_verify_rows(const VerifyArgs& a, int rtw, bool priv, hipStream_t s) {
     if (rtw < 1 || rtw > rows_max_row_tiles(a.d)) return hipErrorInvalidValue;
+    if (priv && !rows_private_waves(a.d, rtw)) return hipErrorInvalidValue;
     switch (a.d * 4 + rtw) {
-        case 64 * 4 + 1: return launch_items(k_verify_rows<64, 1>, a, s, 512);
-        case 64 * 4 + 2: return launch_items(k_verify_rows<64, 2>, a, s, 512);
-        case 96 * 4 + 1: return launch_items(k_verify_rows<96, 1>, a, s, 512);
-        case 128 * 4 + 1: return launch_items(k_verify_rows<128, 1>, a, s, 512);
-        case 128 * 4 + 2: return launch_items(k_verify_rows<128, 2>, a, s, 512);
+        case 64 * 4 + 1:
+            return priv ? launch_items(k_verify_rows<64, 1, true>, a, s, 768)
+                        : launch_items(k_verify_rows<64, 1, false>, a, s, 512);
+        case 64 * 4 + 2:
+            return priv ? launch_items(k_verify_rows<64, 2, true>, a, s, 768)
+                        : launch_items(k_verify_rows<64, 2, false>, a, s, 512);
+        case 96 * 4 + 1:
+            return priv ? launch_items(k_verify_rows<96, 1, true>, a, s, 768)
+                        : launch_items(k_verify_rows<96, 1, false>, a, s, 512);
+        case 128 * 4 + 1: return launch_items(k_verify_rows<128, 1, false>, a, s, 512);
+        case 128 * 4 + 2: return launch_items(k_verify_rows<128, 2, false>, a, s, 512);
     }
     return hipErrorInvalidValue;
 }
