@@ -692,28 +692,41 @@ __device__ __attribute__((always_inline)) inline void private_wave(const VerifyA
     constexpr bool kBlkPf = D * RTW <= 96;
     const bool pf_ok = kBlkPf && it.last && nloops <= 2 && blk_im[0] < 8 && blk_im[1] < 8;
     uint4 pfb[2][PB];
+    auto prefetch_block = [&]() {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const uint16_t* pbk = a.bk.p + it.b * a.bk.sb + (int64_t)(max(blk_r[p], 1) - 1) * a.bk.sp + it.g * a.bk.sh;
-        const uint16_t* pbv = a.bv.p + it.b * a.bv.sb + (int64_t)(max(blk_r[p], 1) - 1) * a.bv.sp + it.g * a.bv.sh;
+        for (int p = 0; p < 2; ++p) {
+            const uint16_t* pbk = a.bk.p + it.b * a.bk.sb + (int64_t)(max(blk_r[p], 1) - 1) * a.bk.sp + it.g * a.bk.sh;
+            const uint16_t* pbv = a.bv.p + it.b * a.bv.sb + (int64_t)(max(blk_r[p], 1) - 1) * a.bv.sp + it.g * a.bv.sh;
 #pragma unroll
-        for (int k = 0; k < PB; ++k) {
-            const int pc = lane + 64 * k;
-            const int c8 = pc % (D / 8), rest = pc / (D / 8);
-            const int key = rest % 8, kv = rest / 8;
-            pfb[p][k] = make_uint4(0, 0, 0, 0);
-            if (pf_ok && p < nloops && key < a.n_blk && key <= blk_im[p])
-                pfb[p][k] = *reinterpret_cast<const uint4*>((kv ? pbv + key * a.bv.st : pbk + key * a.bk.st) + c8 * 8);
+            for (int k = 0; k < PB; ++k) {
+                const int pc = lane + 64 * k;
+                const int c8 = pc % (D / 8), rest = pc / (D / 8);
+                const int key = rest % 8, kv = rest / 8;
+                pfb[p][k] = make_uint4(0, 0, 0, 0);
+                if (pf_ok && p < nloops && key < a.n_blk && key <= blk_im[p])
+                    pfb[p][k] = *reinterpret_cast<const uint4*>((kv ? pbv + key * a.bv.st : pbk + key * a.bk.st) + c8 * 8);
+            }
         }
-    }
+    };
+    // The ring jobs are spread over the loop, sp steps apart: job m is loaded
+    // right after job m - 1 is computed (the first after the first barrier,
+    // so it does not join the start-up burst of deep tiles) and computed sp
+    // steps later; the block rows are requested four steps before the end.
+    const int sp = n_jobs > 0 ? min(4, max(2, n_iter / n_jobs)) : 2;
+    const int pf_step = max(0, n_iter - 4);
     int done = 0;
-    if (n_jobs > 0) load_job(0);
     for (int k = 0; k < n_iter; ++k) {
         asm volatile("s_barrier" ::: "memory");
-        if ((k & 1) == 1 && done < n_jobs) {
+        if (k == 0 && n_jobs > 0) load_job(0);
+        if (k % sp == sp - 1 && done < n_jobs) {
             run_job();
             if (++done < n_jobs) load_job(done);
         }
+        if (k == pf_step) prefetch_block();
+    }
+    if (n_iter == 0) {
+        if (n_jobs > 0) load_job(0);
+        prefetch_block();
     }
     while (done < n_jobs) {
         run_job();
