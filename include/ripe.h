@@ -73,7 +73,8 @@ typedef struct {
     int32_t head_dim;   /* d: 64, 96 or 128 */
     int32_t window;     /* W >= 0, or RIPE_WINDOW_FULL */
     int32_t batch;      /* B sequences, 1..4096 */
-    int32_t capacity;   /* committed positions a sequence may hold, >= 1 */
+    int32_t capacity;   /* committed positions a sequence may hold, >= 1, with
+                           capacity/4 + (R-1)*min(W, capacity)/4 < 2^31 - 2R */
     int32_t max_block;  /* largest draft block (n_blk) a verify call may use, 1..256 */
     int32_t anchor;     /* ripe_anchor */
 } ripe_config;

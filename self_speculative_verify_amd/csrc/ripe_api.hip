@@ -37,7 +37,11 @@ bool valid_config(const ripe_config* c) {
     // element counts must stay far from int64 overflow
     const double elems = (double)c->n_layers * c->batch * c->n_heads_kv * c->head_dim *
                          ((double)c->capacity + 32.0) * c->n_loops;
-    return elems < 4.0e15;
+    // an append launch indexes its 4-position groups of all planes in one
+    // grid dimension
+    const double groups = (c->capacity / 4.0 + 2.0) +
+                          (c->n_loops - 1) * (std::min<double>(c->window, c->capacity) / 4.0 + 2.0);
+    return elems < 4.0e15 && groups < 2147483647.0;
 }
 
 Geometry geometry(const ripe_config* c) {
@@ -304,34 +308,22 @@ ripe_status ripe_append(ripe_cache* cache, int32_t layer, const int32_t* h_n_new
     }
     a.Hkv = g.Hkv; a.d = g.d; a.NR = (int32_t)g.NR;
     a.CP = g.CP; a.WR = g.WR; a.WP = g.WP;
-    const int64_t per_tok = (int64_t)g.Hkv * (g.d / 8);
+    const bool ring = g.NR > 0 && g.WR > 0;
     for (int b0 = 0; b0 < g.B; b0 += ripe::kMaxBatchPerLaunch) {
         a.b0 = b0;
         a.nb = std::min(ripe::kMaxBatchPerLaunch, g.B - b0);
-        int64_t pd = 0;
-        bool any = false;
+        a.gd = 0;
+        a.gr = 0;
         for (int s = 0; s < a.nb; ++s) {
             a.n_new[s] = h_n_new[b0 + s];
             a.L0[s] = lens[b0 + s];
-            a.n_win[s] = (int32_t)std::min<int64_t>(a.n_new[s], g.WR);
-            a.prefix[s] = pd;
-            pd += (int64_t)a.n_new[s] * per_tok;
-            any = any || a.n_new[s] > 0;
+            a.n_win[s] = ring ? (int32_t)std::min<int64_t>(a.n_new[s], g.WR) : 0;
+            a.gd = std::max(a.gd, ripe::append_groups(a.L0[s], a.n_new[s]));
+            a.gr = (int32_t)std::max<int64_t>(
+                a.gr, ripe::append_groups((int64_t)a.L0[s] + a.n_new[s] - a.n_win[s], a.n_win[s]));
         }
-        a.prefix[a.nb] = pd;
-        if (!any) continue;
-        a.total = pd;
-        if (ripe::launch_append_deep(a, stream) != hipSuccess) return RIPE_EDEVICE;
-        if (g.NR > 0 && g.WR > 0) {
-            int64_t pr = 0;
-            for (int s = 0; s < a.nb; ++s) {
-                a.prefix[s] = pr;
-                pr += (int64_t)a.n_win[s] * g.NR * per_tok;
-            }
-            a.prefix[a.nb] = pr;
-            a.total = pr;
-            if (pr > 0 && ripe::launch_append_ring(a, stream) != hipSuccess) return RIPE_EDEVICE;
-        }
+        if (a.gd == 0) continue;
+        if (ripe::launch_append(a, stream) != hipSuccess) return RIPE_EDEVICE;
     }
     for (int b = 0; b < g.B; ++b) lens[b] += h_n_new[b];
     return RIPE_OK;

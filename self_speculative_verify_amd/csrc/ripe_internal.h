@@ -54,15 +54,22 @@ struct AppendArgs {
     int64_t CP, WR, WP;
     int32_t nb;          // sequences in this launch
     int32_t b0;          // first sequence
-    int64_t total;       // work items of this launch
+    // most 4-position groups that any sequence's new positions (gd) and new
+    // window positions (gr, 0 when R = 1 or WR = 0) touch
+    int64_t gd;
+    int32_t gr;
     int32_t n_new[kMaxBatchPerLaunch];
     int32_t L0[kMaxBatchPerLaunch];
     int32_t n_win[kMaxBatchPerLaunch];
-    int64_t prefix[kMaxBatchPerLaunch + 1];   // per-sequence work-item prefix
 };
 
-hipError_t launch_append_deep(const AppendArgs& a, hipStream_t s);
-hipError_t launch_append_ring(const AppendArgs& a, hipStream_t s);
+// groups of 4 positions (aligned to multiples of 4) that the positions
+// [first, first + count) touch
+inline int64_t append_groups(int64_t first, int64_t count) {
+    return count > 0 ? (first + count - 1) / 4 - first / 4 + 1 : 0;
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- verify
 
