@@ -67,7 +67,7 @@ struct Frags {
 template <int D>
 struct RowTile {
     uint4 q[D / 32];      // B operand of S^T: row-head n, dims 32c + 8q..+8
-    float m, l;           // running max of the raw scores and partial sum of p
+    float m, l;           // exponent reference (log2 units, at most the running max) and sum of p
     f32x4 o[D / 16];      // O^T: dims 16dt + 4q..+4 of row-head n
     int ri;               // bits 0..7 block offset, 8..15 loop, bit 16 valid
     int e;                // loop-R positions of this row-head end here (e_row)
@@ -149,111 +149,42 @@ __device__ inline void lds_frags<128>(const uint16_t* stage, Frags<128>& f, int 
 }
 #undef RD
 
+// Maximum that propagates NaN (IEEE maximum): the scores are never NaN, and
+// unlike fmaxf it needs no canonicalising moves, so two or three operands take
+// one v_maximum3_f32.
+__device__ inline float fmaxp(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+__device__ inline float max8(const float (&x)[8]) {
+    return fmaxp(fmaxp(fmaxp(x[0], x[1]), fmaxp(x[2], x[3])), fmaxp(fmaxp(x[4], x[5]), fmaxp(x[6], x[7])));
+}
+
 // max over lanes l, l^16, l^32, l^48 (the four copies of a row-head)
 __device__ inline float max_lane_groups(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = fmaxp(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return fmaxp(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// One key tile against one row tile.  Scores stay in raw units; c = log2(e)/sqrt(d)
-// is folded into the exponent, p = 2^(s*c - m*c).  `full`: every key of the
-// tile is valid for every row-head of the tile (no masking needed).
+// Scores are kept in log2 units, x = s c with c = log2(e)/sqrt(d), and so is
+// a row-head's exponent reference m: p = 2^(x - m).  The reference trails the
+// running maximum: it moves only when a tile's maximum passes it by more than
+// kLazyLog2, so every p stays below 2^kLazyLog2, and l and O are rescaled only
+// then (a row-head's first tile and rare outliers) instead of whenever the
+// maximum grows.  O = sum p v / l and LSE = (m + log2 l) ln 2 hold for any
+// reference, and fp32 keeps l and O exact enough at that scale.
+constexpr float kLazyLog2 = 8.f;
+
+// Moves the references that the tile maximum bm passes by more than the margin
+// (bm = -inf never does) and rescales l and O there by 2^(m_old - m_new): 0 on
+// a row-head's first keys, where l and O are still 0.
 template <int D>
-__device__ inline void tile_update(RowTile<D>& rt, const Frags<D>& f, bool full,
-                                   const bool (&valid)[8], float c) {
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < D / 32; ++k) {
-        s0 = mfma(f.k[k][0], rt.q[k], s0);
-        s1 = mfma(f.k[k][1], rt.q[k], s1);
-    }
-    float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    if (!full) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = valid[e] ? x[e] : -INFINITY;
-    }
-    float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    bm = max_lane_groups(bm);
+__device__ inline void lazy_rescale(RowTile<D>& rt, float bm) {
     const float mo = rt.m;
-    const float mn = fmaxf(mo, bm);
-    const float ms = mn == -INFINITY ? 0.f : mn;     // finite reference for the exponents
-    const float nmc = -ms * c;
-    // exactly 1 when the max did not move (mo - ms == 0), so l and O stay in step
-    const float alpha = __builtin_amdgcn_exp2f((mo - ms) * c);
-    float p[8], ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c, nmc));
-        ps += p[e];
-    }
-    rt.m = mn;
-    rt.l = fmaf(rt.l, alpha, ps);
-    // P = hi + lo, both bf16: hi = round(p), lo = round(p - hi)
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-        hi[e2] = pack_bf16(p[2 * e2], p[2 * e2 + 1]);
-        const float h0 = __uint_as_float(hi[e2] << 16), h1 = __uint_as_float(hi[e2] & 0xffff0000u);
-        lo[e2] = pack_bf16(p[2 * e2] - h0, p[2 * e2 + 1] - h1);
-    }
-    const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    if (__any(mo != mn)) {
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            rt.o[dt][0] *= alpha; rt.o[dt][1] *= alpha;
-            rt.o[dt][2] *= alpha; rt.o[dt][3] *= alpha;
-        }
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-        rt.o[dt] = mfma(f.v[dt], phi, rt.o[dt]);
-        rt.o[dt] = mfma(f.v[dt], plo, rt.o[dt]);
-    }
-}
-
-// S^T = K.Q^T of one key tile against one row tile: lane n, register e holds
-// the raw score of key key_of(e, q) for row-head n
-template <int D>
-__device__ inline void tile_scores(const RowTile<D>& rt, const Frags<D>& f, float (&x)[8]) {
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < D / 32; ++k) {
-        s0 = mfma(f.k[k][0], rt.q[k], s0);
-        s1 = mfma(f.k[k][1], rt.q[k], s1);
-    }
-    x[0] = s0[0]; x[1] = s0[1]; x[2] = s0[2]; x[3] = s0[3];
-    x[4] = s1[0]; x[5] = s1[1]; x[6] = s1[2]; x[7] = s1[3];
-}
-
-// The rest of tile_update for a key tile every row-head of the row tile reads
-// in full: no masks, every score finite, and the rescale of l and O (with its
-// exponential) only when some row-head's max moved.  Uses only f.v.
-template <int D>
-__device__ inline void tile_finish_full(RowTile<D>& rt, const Frags<D>& f, const float (&x)[8], float c) {
-    float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    bm = max_lane_groups(bm);
-    const float mo = rt.m;
-    const float mn = fmaxf(mo, bm);
-    const float nmc = -mn * c;
-    float p[8], ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c, nmc));
-        ps += p[e];
-    }
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-        hi[e2] = pack_bf16(p[2 * e2], p[2 * e2 + 1]);
-        const float h0 = __uint_as_float(hi[e2] << 16), h1 = __uint_as_float(hi[e2] & 0xffff0000u);
-        lo[e2] = pack_bf16(p[2 * e2] - h0, p[2 * e2 + 1] - h1);
-    }
-    if (__any(mo != mn)) {
-        // 2^((mo - mn) c): 0 on the first tile (mo = -inf), exactly 1 where the max stayed
-        const float alpha = __builtin_amdgcn_exp2f((mo - mn) * c);
+    const bool up = bm - mo > kLazyLog2;
+    if (__any(up)) {
+        const float alpha = up ? __builtin_amdgcn_exp2f(mo - bm) : 1.f;
+        rt.m = up ? bm : mo;
         rt.l *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
@@ -261,37 +192,19 @@ __device__ inline void tile_finish_full(RowTile<D>& rt, const Frags<D>& f, const
             rt.o[dt][2] *= alpha; rt.o[dt][3] *= alpha;
         }
     }
-    rt.m = mn;
-    rt.l += ps;
-    const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) rt.o[dt] = mfma(f.v[dt], phi, rt.o[dt]);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) rt.o[dt] = mfma(f.v[dt], plo, rt.o[dt]);
 }
 
-// the rest of tile_update with masks (invalid keys get -inf); uses only f.v
+// p = 2^(x - m) of a lane's 8 scores against the finite reference m, added
+// to l, and O += P V with P split into bf16 hi = round(p) and lo = round(p - hi)
 template <int D>
-__device__ inline void tile_finish_masked(RowTile<D>& rt, const Frags<D>& f, float (&x)[8],
-                                          const bool (&valid)[8], float c) {
+__device__ inline void accumulate(RowTile<D>& rt, const Frags<D>& f, const float (&x)[8], float m) {
+    float p[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = valid[e] ? x[e] : -INFINITY;
-    float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    bm = max_lane_groups(bm);
-    const float mo = rt.m;
-    const float mn = fmaxf(mo, bm);
-    const float ms = mn == -INFINITY ? 0.f : mn;     // finite reference for the exponents
-    const float nmc = -ms * c;
-    const float alpha = __builtin_amdgcn_exp2f((mo - ms) * c);
-    float p[8], ps = 0.f;
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - m);
+    float ps = p[0];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c, nmc));
-        ps += p[e];
-    }
-    rt.m = mn;
-    rt.l = fmaf(rt.l, alpha, ps);
+    for (int e = 1; e < 8; ++e) ps += p[e];
+    rt.l += ps;
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
@@ -301,17 +214,61 @@ __device__ inline void tile_finish_masked(RowTile<D>& rt, const Frags<D>& f, flo
     }
     const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    if (__any(mo != mn)) {
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            rt.o[dt][0] *= alpha; rt.o[dt][1] *= alpha;
-            rt.o[dt][2] *= alpha; rt.o[dt][3] *= alpha;
-        }
-    }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) rt.o[dt] = mfma(f.v[dt], phi, rt.o[dt]);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) rt.o[dt] = mfma(f.v[dt], plo, rt.o[dt]);
+}
+
+// S^T = K.Q^T of one key tile against one row tile: lane n, register e holds
+// the score of key key_of(e, q) for row-head n, times c = log2(e)/sqrt(d).
+// The scaling reads the matrix results in the block that computes them, so
+// the wait they need is never left to a path that branches past it.
+template <int D>
+__device__ inline void tile_scores(const RowTile<D>& rt, const Frags<D>& f, float (&x)[8], float c) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+        s0 = mfma(f.k[k][0], rt.q[k], s0);
+        s1 = mfma(f.k[k][1], rt.q[k], s1);
+    }
+    x[0] = s0[0] * c; x[1] = s0[1] * c; x[2] = s0[2] * c; x[3] = s0[3] * c;
+    x[4] = s1[0] * c; x[5] = s1[1] * c; x[6] = s1[2] * c; x[7] = s1[3] * c;
+}
+
+// The rest of a tile for a key tile every row-head of the row tile reads in
+// full: no masks, every score finite (so every reference is finite after the
+// rescale).  Uses only f.v.
+template <int D>
+__device__ inline void tile_finish_full(RowTile<D>& rt, const Frags<D>& f, const float (&x)[8]) {
+    lazy_rescale<D>(rt, max_lane_groups(max8(x)));
+    accumulate<D>(rt, f, x, rt.m);
+}
+
+// the rest of a tile with masks (invalid keys get -inf; a row-head that has
+// seen no valid key keeps m = -inf and takes p = 0); uses only f.v
+template <int D>
+__device__ inline void tile_finish_masked(RowTile<D>& rt, const Frags<D>& f, float (&x)[8],
+                                          const bool (&valid)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = valid[e] ? x[e] : -INFINITY;
+    lazy_rescale<D>(rt, max_lane_groups(max8(x)));
+    accumulate<D>(rt, f, x, rt.m == -INFINITY ? 0.f : rt.m);   // finite reference
+}
+
+// One key tile against one row tile.  `full`: every key of the tile is valid
+// for every row-head of the tile (no masking needed).
+template <int D>
+__device__ inline void tile_update(RowTile<D>& rt, const Frags<D>& f, bool full,
+                                   const bool (&valid)[8], float c) {
+    float x[8];
+    tile_scores<D>(rt, f, x, c);
+    if (!full) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = valid[e] ? x[e] : -INFINITY;
+    }
+    lazy_rescale<D>(rt, max_lane_groups(max8(x)));
+    accumulate<D>(rt, f, x, rt.m == -INFINITY ? 0.f : rt.m);   // finite reference
 }
 
 // ---------------------------------------------------------------- item// ---------------------------------------------------------------- item
@@ -481,7 +438,7 @@ __device__ inline void write_result_word(const VerifyArgs& a, const Item& it, co
             *reinterpret_cast<float4*>(op + dt * 16 + 4 * q) =
                 make_float4(rt.o[dt][0] * inv, rt.o[dt][1] * inv, rt.o[dt][2] * inv, rt.o[dt][3] * inv);
         if (q == 0)
-            a.lse[((int64_t)it.b * a.n_rows + orig) * a.Hq + h] = (rt.m * a.scale_log2 + log2f(rt.l)) * kLn2;
+            a.lse[((int64_t)it.b * a.n_rows + orig) * a.Hq + h] = (rt.m + log2f(rt.l)) * kLn2;
     } else {
         const int64_t pidx = (((int64_t)it.b * a.Hkv + it.g) * a.nc + it.c) * a.M + u;
         float* po = a.part + pidx * (D + 2);
@@ -490,8 +447,8 @@ __device__ inline void write_result_word(const VerifyArgs& a, const Item& it, co
             *reinterpret_cast<float2*>(po + dt * 16 + 4 * q) = make_float2(rt.o[dt][0], rt.o[dt][1]);
             *reinterpret_cast<float2*>(po + dt * 16 + 4 * q + 2) = make_float2(rt.o[dt][2], rt.o[dt][3]);
         }
-        // partial max in the log2 domain (-inf stays -inf)
-        if (q == 0) *reinterpret_cast<float2*>(po + D) = make_float2(rt.m * a.scale_log2, rt.l);
+        // partial reference in the log2 domain (-inf stays -inf)
+        if (q == 0) *reinterpret_cast<float2*>(po + D) = make_float2(rt.m, rt.l);
     }
 }
 template <int D>
@@ -1112,10 +1069,10 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
         advance(j);
         float x[RTW][8];
 #pragma unroll
-        for (int tr = 0; tr < RTW; ++tr) tile_scores<D>(rt[tr], f, x[tr]);
+        for (int tr = 0; tr < RTW; ++tr) tile_scores<D>(rt[tr], f, x[tr], sl2);
         next_keys(j);
 #pragma unroll
-        for (int tr = 0; tr < RTW; ++tr) tile_finish_full<D>(rt[tr], f, x[tr], sl2);
+        for (int tr = 0; tr < RTW; ++tr) tile_finish_full<D>(rt[tr], f, x[tr]);
         next_values(j);
     }
     // general phase: deep tiles with masks, then ring tiles
@@ -1153,12 +1110,12 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
         }
 #pragma unroll
         for (int tr = 0; tr < RTW; ++tr)
-            if (mode[tr]) tile_scores<D>(rt[tr], f, x[tr]);
+            if (mode[tr]) tile_scores<D>(rt[tr], f, x[tr], sl2);
         next_keys(j);
 #pragma unroll
         for (int tr = 0; tr < RTW; ++tr) {
-            if (mode[tr] == 2) tile_finish_full<D>(rt[tr], f, x[tr], sl2);
-            else if (mode[tr] == 1) tile_finish_masked<D>(rt[tr], f, x[tr], v[tr], sl2);
+            if (mode[tr] == 2) tile_finish_full<D>(rt[tr], f, x[tr]);
+            else if (mode[tr] == 1) tile_finish_masked<D>(rt[tr], f, x[tr], v[tr]);
         }
         next_values(j);
     }
@@ -1236,8 +1193,8 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
                 const float* src = s_m + (src_i * 4 * RTW * 64 + (rw * RTW + tr) * 64 + lane) * MS;
                 const float m2 = src[D / 4], l2 = src[D / 4 + 1];
                 const float mn = fmaxf(rt[tr].m, m2);
-                const float w1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((rt[tr].m - mn) * sl2);
-                const float w2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * sl2);
+                const float w1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rt[tr].m - mn);
+                const float w2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
                 rt[tr].m = mn;
                 rt[tr].l = rt[tr].l * w1 + l2 * w2;
 #pragma unroll
@@ -1503,8 +1460,8 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
         for (int tr = 0; tr < RT; ++tr) {
             const float m2 = s_st[buf][tr][n][D], l2 = s_st[buf][tr][n][D + 1];
             const float mn = fmaxf(rt[tr].m, m2);
-            const float w1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((rt[tr].m - mn) * a.scale_log2);
-            const float w2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m2 - mn) * a.scale_log2);
+            const float w1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rt[tr].m - mn);
+            const float w2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
             rt[tr].m = mn;
             rt[tr].l = rt[tr].l * w1 + l2 * w2;
 #pragma unroll
