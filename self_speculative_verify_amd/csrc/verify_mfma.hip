@@ -245,6 +245,38 @@ __device__ inline void tile_finish_full(RowTile<D>& rt, const Frags<D>& f, const
     accumulate<D>(rt, f, x, rt.m);
 }
 
+// tile_finish_full for all row tiles of a wave at once: one rescale test for
+// all of them, then every tile's exponentials and matrix products in one
+// block, so the products of one row tile can run beside the exponentials of
+// the next.
+template <int D, int RT>
+__device__ inline void tiles_finish_full(RowTile<D> (&rt)[RT], const Frags<D>& f, const float (&x)[RT][8]) {
+    float bm[RT];
+    bool up[RT], any = false;
+#pragma unroll
+    for (int tr = 0; tr < RT; ++tr) {
+        bm[tr] = max_lane_groups(max8(x[tr]));
+        up[tr] = bm[tr] - rt[tr].m > kLazyLog2;
+        any = any || up[tr];
+    }
+    if (__any(any)) {
+#pragma unroll
+        for (int tr = 0; tr < RT; ++tr) {
+            const float mo = rt[tr].m;
+            const float alpha = up[tr] ? __builtin_amdgcn_exp2f(mo - bm[tr]) : 1.f;
+            rt[tr].m = up[tr] ? bm[tr] : mo;
+            rt[tr].l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                rt[tr].o[dt][0] *= alpha; rt[tr].o[dt][1] *= alpha;
+                rt[tr].o[dt][2] *= alpha; rt[tr].o[dt][3] *= alpha;
+            }
+        }
+    }
+#pragma unroll
+    for (int tr = 0; tr < RT; ++tr) accumulate<D>(rt[tr], f, x[tr], rt[tr].m);
+}
+
 // the rest of a tile with masks (invalid keys get -inf; a row-head that has
 // seen no valid key keeps m = -inf and takes p = 0); uses only f.v
 template <int D>
@@ -1071,8 +1103,7 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
 #pragma unroll
         for (int tr = 0; tr < RTW; ++tr) tile_scores<D>(rt[tr], f, x[tr], sl2);
         next_keys(j);
-#pragma unroll
-        for (int tr = 0; tr < RTW; ++tr) tile_finish_full<D>(rt[tr], f, x[tr]);
+        tiles_finish_full<D, RTW>(rt, f, x);
         next_values(j);
     }
     // general phase: deep tiles with masks, then ring tiles
