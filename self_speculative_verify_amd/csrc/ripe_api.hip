@@ -166,7 +166,11 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
     // workgroups of one (sequence, chunk) pair, and of the whole call unsplit
     const int64_t units = (int64_t)g.Hkv * p.nrb;
     const int64_t base = g.B * units;
-    const int64_t slots = draft ? 0 : target_env ? target_env : (p.rows_kernel ? 256 : 512);
+    // workgroup target: one round of the rows kernel; for the keys kernel
+    // (two workgroups per CU) a second round only pays off on long contexts,
+    // where the chunks stay long enough to outweigh the extra partial states
+    const int64_t slots = draft ? 0 : target_env ? target_env
+                                    : (p.rows_kernel || lmax <= 4096 ? 256 : 512);
     const int64_t cx = 32 * extra_tiles(g, rows, rows_here, p.M, p.nrb, rows_per_item, lmax);
     const int64_t min_chunk = force_min_chunk ? force_min_chunk : std::max<int64_t>(256, 8 * rows_per_item);
     // One chunk length for every sequence, from their total: the pairs that
