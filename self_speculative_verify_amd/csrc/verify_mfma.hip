@@ -594,10 +594,11 @@ __device__ inline void lds_values(const uint16_t* stage, Frags<D>& f, int lane) 
 // LDS stages of the rows kernel's tile stream (one tile pair per key half
 // each): 128 / 144 / 128 KB
 constexpr int rows_stages(int d) { return d == 128 ? 4 : (d == 96 ? 6 : 8); }
-// a barrier every second step where the stages allow two tiles to be
-// consumed per barrier while three or more are in flight (measured: the
-// Huginn-scale launch 4% faster; with four stages at head_dim 128, 5% slower)
-constexpr bool rows_pair_steps(int d) { return rows_stages(d) >= 6; }
+// steps per barrier where the stages allow: K tiles consumed per barrier
+// while the next ones load (measured on the Huginn-scale launch: two steps
+// 4% and three steps 11% faster than one; with the four stages of head_dim
+// 128, two steps were 5% slower)
+constexpr int rows_barrier_steps(int d) { return rows_stages(d) >= 6 ? 3 : 1; }
 
 template <int D, int RTW>
 __device__ __attribute__((always_inline)) inline void private_wave(const VerifyArgs& a, const Item& it,
@@ -713,7 +714,7 @@ __device__ __attribute__((always_inline)) inline void private_wave(const VerifyA
     const int pf_step = max(0, n_iter - 4);
     int done = 0;
     for (int k = 0; k < n_iter; ++k) {
-        if (!rows_pair_steps(D) || (k & 1) == 0) asm volatile("s_barrier" ::: "memory");   // the main waves' barriers
+        if (k % rows_barrier_steps(D) == 0) asm volatile("s_barrier" ::: "memory");   // the main waves' barriers
         if (k == 0 && n_jobs > 0) load_job(0);
         if (k % sp == sp - 1 && done < n_jobs) {
             run_job();
@@ -833,7 +834,11 @@ template <int D, int RTW, bool PRIV>
 __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs a) {
     constexpr int TILE = 32 * D;                 // elements of one K or V tile
     constexpr int S = rows_stages(D);
-    constexpr bool kPair = rows_pair_steps(D);
+    constexpr int K = rows_barrier_steps(D);
+    // tiles loaded ahead of the first step: as many as leave the stages of
+    // the K tiles consumed before each barrier free for the next K
+    constexpr int P = K == 1 ? S - 1 : S - K + 1;
+    static_assert(P >= K + 1, "the K tiles after a barrier must be loaded by then");
     constexpr int PT = D / 32;                   // direct loads per thread per tile pair
     constexpr int PF = D / 16;                   // prefetched draft-block pieces per lane
     constexpr int MS = D / 4 + 2;                // floats of one lane's state in the merge
@@ -1000,11 +1005,11 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
         ti += 2;
         ++issued;
     };
-    static_assert((S - 2) * PT <= 63, "vmcnt field");
+    static_assert((P - 1) * PT <= 15, "vmcnt field");
 
-    // the first S - 1 tile pairs of this half (after the query loads, so the
-    // wait for tile 0 covers them)
-    for (int j = 0; j < S - 1; ++j) {
+    // the first P tile pairs of this half (after the query loads, so the wait
+    // for tile 0 covers them)
+    for (int j = 0; j < P; ++j) {
         if (ti < n_tiles) issue_next(s_tile[j][kh]);
         else issue_dummy(s_tile[j][kh]);
     }
@@ -1067,7 +1072,7 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
     // after this barrier the queries and every wave's part of tile 0 are in
     // LDS (the S - 2 groups issued after tile 0 may be outstanding); the asm
     // text differs from the loop's barrier so the two are never merged
-    __builtin_amdgcn_s_waitcnt(0xF70 | ((S - 2) * PT));
+    __builtin_amdgcn_s_waitcnt(0xF70 | ((P - 1) * PT));
     asm volatile("s_barrier ; queries and tile 0" ::: "memory");
 #pragma unroll
     for (int t = 0; t < RTW; ++t)
@@ -1079,24 +1084,22 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
     }
     int sj = 0;                                   // stage of tile j
     int sn = 1;                                   // stage of tile j + 1
-    // kPair: a barrier every second step.  At an even step j every wave waits
-    // for its parts of tiles j + 1 and j + 2, the barrier makes them visible
-    // (and every wave has read tile j by then), and tiles j + S - 1 and j + S
-    // go into the stages of tiles j - 1 and j.  The odd steps run without a
-    // barrier, so the waves sharing a SIMD can drift apart by a tile.
-    // Otherwise a barrier every step: tile j + 1 in LDS for every wave, every
-    // wave's reads of tile j - 1 done, tile j + S - 1 into its stage.
+    // A barrier every K steps.  At a step j that is a multiple of K every wave
+    // waits for its parts of tiles j + 1 .. j + K, the barrier makes them
+    // visible (and every wave has read tiles up to j by then), and the next K
+    // tiles of the stream go into the stages of tiles j - K + 1 .. j.  Between
+    // barriers the waves sharing a SIMD can drift apart.
     auto advance = [&](int j) {
-        if (kPair && (j & 1)) return;
-        __builtin_amdgcn_s_waitcnt(0xF70 | ((kPair ? S - 4 : S - 3) * PT));
+        if (K > 1 && j % K) return;
+        __builtin_amdgcn_s_waitcnt(0xF70 | ((P - 1 - K) * PT));
         asm volatile("s_barrier" ::: "memory");
-        uint16_t* sp = s_tile[sj == 0 ? S - 1 : sj - 1][kh];   // stage of tile j - 1
-        if (ti < n_tiles) issue_next(sp);
-        else issue_dummy(sp);
-        if (kPair) {
-            uint16_t* sc = s_tile[sj][kh];                      // stage of tile j
-            if (ti < n_tiles) issue_next(sc);
-            else issue_dummy(sc);
+        // tile m of the stream lives in stage m mod S; the next K tiles,
+        // P + j .. P + j + K - 1, replace tiles consumed by now
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int st = (sj + P + k) % S;       // sj = j mod S
+            if (ti < n_tiles) issue_next(s_tile[st][kh]);
+            else issue_dummy(s_tile[st][kh]);
         }
     };
     auto next_keys = [&](int j) {
