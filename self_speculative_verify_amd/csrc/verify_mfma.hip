@@ -592,12 +592,13 @@ __device__ inline void lds_values(const uint16_t* stage, Frags<D>& f, int lane) 
 // It executes exactly the barriers of the other waves: one before the loop,
 // n_iter in it, four after it.
 // LDS stages of the rows kernel's tile stream (one tile pair per key half
-// each): 128 / 144 / 128 KB
-constexpr int rows_stages(int d) { return d == 128 ? 4 : (d == 96 ? 6 : 8); }
+// each; the query operands borrow the last stage until the first step):
+// 160 / 144 / 160 KB
+constexpr int rows_stages(int d) { return d == 128 ? 5 : (d == 96 ? 6 : 10); }
 // steps per barrier where the stages allow: K tiles consumed per barrier
 // while the next ones load (measured on the Huginn-scale launch: two steps
-// 4% and three steps 11% faster than one; with the four stages of head_dim
-// 128, two steps were 5% slower)
+// 4% and three steps 11% faster than one; at head_dim 128, with four or five
+// stages, two steps were 5% slower)
 constexpr int rows_barrier_steps(int d) { return rows_stages(d) >= 6 ? 3 : 1; }
 
 template <int D, int RTW>
@@ -714,7 +715,7 @@ __device__ __attribute__((always_inline)) inline void private_wave(const VerifyA
     const int pf_step = max(0, n_iter - 4);
     int done = 0;
     for (int k = 0; k < n_iter; ++k) {
-        if (k % rows_barrier_steps(D) == 0) asm volatile("s_barrier" ::: "memory");   // the main waves' barriers
+        if (k % rows_barrier_steps(D) == 0) lds_barrier();   // the main waves' barriers
         if (k == 0 && n_jobs > 0) load_job(0);
         if (k % sp == sp - 1 && done < n_jobs) {
             run_job();
@@ -839,11 +840,16 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
     // the K tiles consumed before each barrier free for the next K
     constexpr int P = K == 1 ? S - 1 : S - K + 1;
     static_assert(P >= K + 1, "the K tiles after a barrier must be loaded by then");
+    static_assert(P <= S - 1, "the last stage holds the queries until the first step");
     constexpr int PT = D / 32;                   // direct loads per thread per tile pair
     constexpr int PF = D / 16;                   // prefetched draft-block pieces per lane
     constexpr int MS = D / 4 + 2;                // floats of one lane's state in the merge
     __shared__ __attribute__((aligned(16))) uint16_t s_tile[S][2][2 * TILE];
-    __shared__ __attribute__((aligned(16))) uint4 s_q[4][RTW * (D / 32)][64];   // query operands per row group
+    // query operands per row group, in the last stage: the first tiles go to
+    // stages 0 .. P - 1 < S - 1, and the last stage's first tile is issued
+    // after the first barrier of the loop, when every wave has read them
+    static_assert(4 * RTW * (D / 32) * 64 * 16 <= (int)sizeof(s_tile[0]), "queries in a stage");
+    uint4 (*const s_q)[RTW * (D / 32)][64] = reinterpret_cast<uint4 (*)[RTW * (D / 32)][64]>(&s_tile[S - 1][0][0]);
     static_assert((PRIV ? 2 : 1) * 4 * RTW * 64 * MS * 4 <= (int)sizeof(s_tile), "merge buffers");
     static_assert(8 * 2 * TILE * 2 <= (int)sizeof(s_tile), "per-wave block scratch");
     static_assert(RTW <= 2, "two row words per lane");
@@ -1091,7 +1097,9 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
     // barriers the waves sharing a SIMD can drift apart.
     auto advance = [&](int j) {
         if (K > 1 && j % K) return;
-        __builtin_amdgcn_s_waitcnt(0xF70 | ((P - 1 - K) * PT));
+        // (and no LDS read of this wave in flight: the first barrier of the
+        // loop frees the queries' stage)
+        __builtin_amdgcn_s_waitcnt(0x070 | ((P - 1 - K) * PT));
         asm volatile("s_barrier" ::: "memory");
         // tile m of the stream lives in stage m mod S; the next K tiles,
         // P + j .. P + j + K - 1, replace tiles consumed by now
