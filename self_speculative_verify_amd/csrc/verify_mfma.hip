@@ -90,65 +90,6 @@ __device__ inline void load_frags(const uint16_t* K, const uint16_t* V, Frags<D>
         f.v[dt] = *reinterpret_cast<const uint4*>(V + (dt * 16 + n) * 32 + 8 * q);
 }
 
-// The same operand pieces from a tile pair staged in LDS by load_stage: piece
-// i of D/8 (K pieces, then V pieces) is a 1 KB block in which lane l's 16
-// bytes sit at l*16, so each ds_read_b128 is one conflict-free contiguous
-// read.  One asm block issues all reads and waits for them, so no output
-// register is live while its load is in flight; the compiler sees no LDS read
-// it could order against the in-flight global->LDS loads of other stages.  The
-// outputs are early-clobber: later reads of the block still use the address.
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-#define RD(i) "ds_read_b128 %" #i ", %[a] offset:" #i "*1024\n"
-template <int D>
-__device__ inline void lds_frags(const uint16_t* stage, Frags<D>& f, int n, int q);
-template <>
-__device__ inline void lds_frags<64>(const uint16_t* stage, Frags<64>& f, int n, int q) {
-    const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)stage + (q * 16 + n) * 16;
-    u32x4 r0, r1, r2, r3, r4, r5, r6, r7;
-    asm volatile(RD(0) RD(1) RD(2) RD(3) RD(4) RD(5) RD(6) RD(7) "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-                 : [a] "v"(addr) : "memory");
-    f.k[0][0] = __builtin_bit_cast(uint4, r0); f.k[0][1] = __builtin_bit_cast(uint4, r1);
-    f.k[1][0] = __builtin_bit_cast(uint4, r2); f.k[1][1] = __builtin_bit_cast(uint4, r3);
-    f.v[0] = __builtin_bit_cast(uint4, r4); f.v[1] = __builtin_bit_cast(uint4, r5);
-    f.v[2] = __builtin_bit_cast(uint4, r6); f.v[3] = __builtin_bit_cast(uint4, r7);
-}
-template <>
-__device__ inline void lds_frags<96>(const uint16_t* stage, Frags<96>& f, int n, int q) {
-    const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)stage + (q * 16 + n) * 16;
-    u32x4 r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11;
-    asm volatile(RD(0) RD(1) RD(2) RD(3) RD(4) RD(5) RD(6) RD(7) RD(8) RD(9) RD(10) RD(11)
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7),
-                   "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11)
-                 : [a] "v"(addr) : "memory");
-    f.k[0][0] = __builtin_bit_cast(uint4, r0); f.k[0][1] = __builtin_bit_cast(uint4, r1);
-    f.k[1][0] = __builtin_bit_cast(uint4, r2); f.k[1][1] = __builtin_bit_cast(uint4, r3);
-    f.k[2][0] = __builtin_bit_cast(uint4, r4); f.k[2][1] = __builtin_bit_cast(uint4, r5);
-    f.v[0] = __builtin_bit_cast(uint4, r6); f.v[1] = __builtin_bit_cast(uint4, r7);
-    f.v[2] = __builtin_bit_cast(uint4, r8); f.v[3] = __builtin_bit_cast(uint4, r9);
-    f.v[4] = __builtin_bit_cast(uint4, r10); f.v[5] = __builtin_bit_cast(uint4, r11);
-}
-template <>
-__device__ inline void lds_frags<128>(const uint16_t* stage, Frags<128>& f, int n, int q) {
-    const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)stage + (q * 16 + n) * 16;
-    u32x4 r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11, r12, r13, r14, r15;
-    asm volatile(RD(0) RD(1) RD(2) RD(3) RD(4) RD(5) RD(6) RD(7) RD(8) RD(9) RD(10) RD(11)
-                 RD(12) RD(13) RD(14) RD(15) "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7),
-                   "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13), "=&v"(r14), "=&v"(r15)
-                 : [a] "v"(addr) : "memory");
-    f.k[0][0] = __builtin_bit_cast(uint4, r0); f.k[0][1] = __builtin_bit_cast(uint4, r1);
-    f.k[1][0] = __builtin_bit_cast(uint4, r2); f.k[1][1] = __builtin_bit_cast(uint4, r3);
-    f.k[2][0] = __builtin_bit_cast(uint4, r4); f.k[2][1] = __builtin_bit_cast(uint4, r5);
-    f.k[3][0] = __builtin_bit_cast(uint4, r6); f.k[3][1] = __builtin_bit_cast(uint4, r7);
-    f.v[0] = __builtin_bit_cast(uint4, r8); f.v[1] = __builtin_bit_cast(uint4, r9);
-    f.v[2] = __builtin_bit_cast(uint4, r10); f.v[3] = __builtin_bit_cast(uint4, r11);
-    f.v[4] = __builtin_bit_cast(uint4, r12); f.v[5] = __builtin_bit_cast(uint4, r13);
-    f.v[6] = __builtin_bit_cast(uint4, r14); f.v[7] = __builtin_bit_cast(uint4, r15);
-}
-#undef RD
-
 // Maximum that propagates NaN (IEEE maximum): the scores are never NaN, and
 // unlike fmaxf it needs no canonicalising moves, so two or three operands take
 // one v_maximum3_f32.
@@ -584,13 +525,6 @@ __device__ inline void lds_values(const uint16_t* stage, Frags<D>& f, int lane) 
     for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = p[(D / 16 + dt) * 64];
 }
 
-// The private wave of row group rw in the rows kernel (PRIV): the ring tiles
-// of the row group's loops while the deep tiles stream (one tile every second
-// step, loaded two steps ahead into registers, so its loads never hold back
-// a barrier), then its draft-block tiles, staged in a wave-private part of
-// the stages once they are free; its state goes to the second merge buffer.
-// It executes exactly the barriers of the other waves: one before the loop,
-// n_iter in it, four after it.
 // LDS stages of the rows kernel's tile stream (one tile pair per key half
 // each; the query operands borrow the last stage until the first step):
 // 160 / 144 / 160 KB
@@ -601,6 +535,14 @@ constexpr int rows_stages(int d) { return d == 128 ? 5 : (d == 96 ? 6 : 10); }
 // stages, two steps were 5% slower)
 constexpr int rows_barrier_steps(int d) { return rows_stages(d) >= 6 ? 3 : 1; }
 
+// The private wave of row group rw in the rows kernel (PRIV): the ring tiles
+// of the row group's loops while the deep tiles stream (spread over the loop,
+// each loaded into registers a few steps before it is computed, so its loads
+// never hold back a barrier), then its draft-block tiles, staged in a
+// wave-private part of the stages once they are free; its state goes to the
+// second merge buffer.
+// It executes exactly the barriers of the other waves: one before the loop,
+// one every rows_barrier_steps steps in it, four after it.
 template <int D, int RTW>
 __device__ __attribute__((always_inline)) inline void private_wave(const VerifyArgs& a, const Item& it,
         RowTile<D> (&rt)[RTW], int rw, int u_w, int n_iter, int ring_tiles, int64_t rreg0,
@@ -817,12 +759,12 @@ __device__ __attribute__((always_inline)) inline void private_wave(const VerifyA
 // two independent tile steps; their softmax states merge through LDS at the end.
 // The stream is the chunk's deep tiles, then the ring tiles of every loop
 // r < R present in the workgroup.  All eight waves load each tile pair into an
-// LDS stage with direct global->LDS loads, S - 2 or more iterations ahead,
-// and read it with asm LDS reads (one barrier per step, or per two steps
-// where the stages allow).  Row data goes from the kernel arguments into registers,
-// and compiler-visible code touches no LDS between the first direct load and
-// the merge, so the compiler never drains the load pipeline; all waits on the
-// direct loads are explicit.  Deep tiles that every row-head reads in full take
+// LDS stage with direct global->LDS loads, two or more steps ahead (a
+// barrier every step, or every third step where the stages allow).  The
+// direct loads are asm, which the compiler does not see writing LDS, so its
+// own LDS reads of the stages never make it drain the load pipeline; every
+// wait on the direct loads is explicit.  Row data goes from the kernel
+// arguments into registers.  Deep tiles that every row-head reads in full take
 // the unmasked step.
 //
 // PRIV: four more waves, one per row group, take the ring and draft-block
