@@ -79,3 +79,14 @@ def test_draft_block_longer_than_a_tile(D):
 @pytest.mark.parametrize("W", [500, WINDOW_FULL])
 def test_window_longer_than_the_capacity(W):
     run(Workload("wcap", 94, 1, 6, 4, 2, 128, W, 4, [120, 300, 33], 0.81, grid_rows(4, 6)))
+
+
+@pytest.mark.parametrize("d,lens", [(64, [1999, 1501]), (96, [2047, 700]), (128, [1500, 333])])
+def test_long_streams_every_head_size(d, lens):
+    """Deep streams of 20-64 tiles per key half at each head size, so the rows
+    kernel's stage pipeline runs through its steady state (barriers every
+    third step at head_dim 64 and 96, every step at 128), with tile counts
+    that end on every phase of the barrier period; 128 or more row-heads per
+    KV head with two heads per group."""
+    rows = grid_rows(8, 8)                       # 64 rows x 2 query heads per KV head
+    run(Workload(f"long{d}", 95 + d, 1, 8, 4, 2, d, 64, 8, lens, 0.88, rows, heavy_frac=0.01))
