@@ -404,6 +404,8 @@ ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32
         for (int k = 0; k < a.rows_here; ++k) a.rows[k] = rows[k0 + k];
         const Plan p = make_plan(g, lens, a.rows_here, a.rows, draft);
         a.M = p.M; a.nrb = p.nrb; a.nc = p.nc; a.cl = p.cl; a.cx = p.cx; a.n_groups = p.n_groups;
+        for (int b = 0; b < ripe::kMaxSeqArgs; ++b)
+            a.snc[b] = b < g.B ? (lens[b] > 0 ? (int32_t)((lens[b] + p.cx + p.cl - 1) / p.cl) : 1) : 0;
         const hipError_t e = p.rows_kernel ? ripe::launch_verify_rows(a, p.rt, p.priv, stream)
                                            : ripe::launch_verify_keys(a, p.rt, stream);
         if (e != hipSuccess) return RIPE_EDEVICE;

@@ -10,6 +10,7 @@ namespace ripe {
 constexpr int kTile = 32;          // rows (positions or ring slots) per tile
 constexpr int kMaxBatchPerLaunch = 64;
 constexpr int kMaxRowsPerLaunch = 256;
+constexpr int kMaxSeqArgs = 64;
 
 // Storage geometry derived from a configuration (all counts, no bytes).
 struct Geometry {
@@ -103,6 +104,10 @@ struct VerifyArgs {
     // rows of this launch sorted by (loop, block offset):
     // bits 0..7 block offset, 8..15 loop, 16..31 row index in the call
     uint32_t rows[kMaxRowsPerLaunch];
+    // chunks of each sequence when the batch has at most kMaxSeqArgs
+    // sequences (0: read the length from storage); the host's copy of the
+    // lengths advances in stream order with the one in storage
+    int32_t snc[kMaxSeqArgs];
 };
 
 // matrix-core kernels: "keys" (waves split the key tiles of 16*rt row-heads)

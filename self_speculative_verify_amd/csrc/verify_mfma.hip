@@ -1498,7 +1498,10 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
 // M = max m_c, l = sum l_c 2^(m_c - M), O = sum O_c 2^(m_c - M) / l.
 // One wave per row-head.  Lane c reads the (m, l) of chunk c, so the chunk
 // states arrive together; the value rows of eight chunks are loaded before
-// any is summed, so the loads overlap instead of forming a chain.
+// any is summed, so the loads overlap instead of forming a chain.  With at
+// most eight chunks (the usual case) the value rows are requested together
+// with the states, and the chunk count comes with the arguments, so the
+// merge waits for one round of loads.
 template <int D>
 __global__ void __launch_bounds__(256) k_combine(VerifyArgs a) {
     const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1508,43 +1511,75 @@ __global__ void __launch_bounds__(256) k_combine(VerifyArgs a) {
     const int u = (int)(idx % a.M);
     const int bg = (int)(idx / a.M);
     const int g = bg % a.Hkv, b = bg / a.Hkv;
-    const int64_t L = a.lens[b];
-    const int nc_b = L > 0 ? (int)((L + a.cx + a.cl - 1) / a.cl) : 1;
+    int nc_b = b < kMaxSeqArgs ? a.snc[b] : 0;
+    if (nc_b == 0) {
+        const int64_t L = a.lens[b];
+        nc_b = L > 0 ? (int)((L + a.cx + a.cl - 1) / a.cl) : 1;
+    }
     if (nc_b == 1) return;
     const int64_t cs = (int64_t)a.M * (D + 2);                  // chunk stride
     const float* pu = a.part + (int64_t)bg * a.nc * cs + (int64_t)u * (D + 2);
-    float mx = -INFINITY;
-    for (int c = lane; c < nc_b; c += 64) mx = fmaxf(mx, pu[c * cs + D]);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     constexpr int NE = (D + 63) / 64;
     constexpr int CB = 8;                                          // chunks per batch of loads
-    float acc[NE], lt = 0.f;
+    float acc[NE], lt = 0.f, mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < NE; ++t) acc[t] = 0.f;
-    for (int c0 = 0; c0 < nc_b; c0 += 64) {
-        float w = 0.f;
-        if (c0 + lane < nc_b) {
-            const float* p = pu + (c0 + lane) * cs;
-            const float m = p[D];
-            w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mx);
-            lt += w * p[D + 1];
+    if (nc_b <= CB) {
+        // every load at once: the (m, l) of chunk `lane` and the value rows
+        // of all chunks (they do not depend on the maximum)
+        float m = -INFINITY, l = 0.f;
+        if (lane < nc_b) {
+            m = pu[lane * cs + D];
+            l = pu[lane * cs + D + 1];
         }
-        const int n = min(64, nc_b - c0);
-        for (int k = 0; k < n; k += CB) {
-            float v[CB][NE];
+        float v[CB][NE];
 #pragma unroll
-            for (int j = 0; j < CB; ++j)
+        for (int j = 0; j < CB; ++j)
 #pragma unroll
-                for (int t = 0; t < NE; ++t) {
-                    const int e = lane + 64 * t;
-                    v[j][t] = (k + j < n && e < D) ? pu[(c0 + k + j) * cs + e] : 0.f;
+            for (int t = 0; t < NE; ++t) {
+                const int e = lane + 64 * t;
+                v[j][t] = (j < nc_b && e < D) ? pu[j * cs + e] : 0.f;
+            }
+        mx = m;
+#pragma unroll
+        for (int o = 1; o < CB; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        mx = __shfl(mx, 0);
+        const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mx);
+        lt = w * l;
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            const float wj = __shfl(w, j);
+#pragma unroll
+            for (int t = 0; t < NE; ++t) acc[t] += wj * v[j][t];
+        }
+    } else {
+        for (int c = lane; c < nc_b; c += 64) mx = fmaxf(mx, pu[c * cs + D]);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        for (int c0 = 0; c0 < nc_b; c0 += 64) {
+            float w = 0.f;
+            if (c0 + lane < nc_b) {
+                const float* p = pu + (c0 + lane) * cs;
+                const float m = p[D];
+                w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mx);
+                lt += w * p[D + 1];
+            }
+            const int n = min(64, nc_b - c0);
+            for (int k = 0; k < n; k += CB) {
+                float v[CB][NE];
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+#pragma unroll
+                    for (int t = 0; t < NE; ++t) {
+                        const int e = lane + 64 * t;
+                        v[j][t] = (k + j < n && e < D) ? pu[(c0 + k + j) * cs + e] : 0.f;
+                    }
+#pragma unroll
+                for (int j = 0; j < CB; ++j) {
+                    const float wj = __shfl(w, k + j);
+#pragma unroll
+                    for (int t = 0; t < NE; ++t) acc[t] += wj * v[j][t];
                 }
-#pragma unroll
-            for (int j = 0; j < CB; ++j) {
-                const float wj = __shfl(w, k + j);
-#pragma unroll
-                for (int t = 0; t < NE; ++t) acc[t] += wj * v[j][t];
             }
         }
     }
