@@ -135,13 +135,14 @@ __device__ inline void lazy_rescale(RowTile<D>& rt, float bm) {
     }
 }
 
-// p = 2^(x - m) of a lane's 8 scores against the finite reference m, added
-// to l, and O += P V with P split into bf16 hi = round(p) and lo = round(p - hi)
+// p = 2^(s c - m) of a lane's 8 raw scores s against the finite reference m
+// (one fma per score), added to l, and O += P V with P split into bf16
+// hi = round(p) and lo = round(p - hi)
 template <int D>
-__device__ inline void accumulate(RowTile<D>& rt, const Frags<D>& f, const float (&x)[8], float m) {
+__device__ inline void accumulate(RowTile<D>& rt, const Frags<D>& f, const float (&x)[8], float c, float m) {
     float p[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - m);
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -m));
     float ps = p[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) ps += p[e];
@@ -162,28 +163,34 @@ __device__ inline void accumulate(RowTile<D>& rt, const Frags<D>& f, const float
 }
 
 // S^T = K.Q^T of one key tile against one row tile: lane n, register e holds
-// the score of key key_of(e, q) for row-head n, times c = log2(e)/sqrt(d).
-// The scaling reads the matrix results in the block that computes them, so
-// the wait they need is never left to a path that branches past it.
+// the raw score of key key_of(e, q) for row-head n (the log2-domain scale
+// c = log2(e)/sqrt(d) is applied in the exponent's fma).  Returns the
+// maximum of the lane's eight scores, computed in the block that runs the
+// matrix instructions: the first reader of their results is then never at
+// the head of a block that a branch reaches straight from them (the compiler
+// left such a path without the wait the results need).
 template <int D>
-__device__ inline void tile_scores(const RowTile<D>& rt, const Frags<D>& f, float (&x)[8], float c) {
+__device__ inline float tile_scores(const RowTile<D>& rt, const Frags<D>& f, float (&x)[8]) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < D / 32; ++k) {
         s0 = mfma(f.k[k][0], rt.q[k], s0);
         s1 = mfma(f.k[k][1], rt.q[k], s1);
     }
-    x[0] = s0[0] * c; x[1] = s0[1] * c; x[2] = s0[2] * c; x[3] = s0[3] * c;
-    x[4] = s1[0] * c; x[5] = s1[1] * c; x[6] = s1[2] * c; x[7] = s1[3] * c;
+    x[0] = s0[0]; x[1] = s0[1]; x[2] = s0[2]; x[3] = s0[3];
+    x[4] = s1[0]; x[5] = s1[1]; x[6] = s1[2]; x[7] = s1[3];
+    return max8(x);
 }
 
 // The rest of a tile for a key tile every row-head of the row tile reads in
 // full: no masks, every score finite (so every reference is finite after the
-// rescale).  Uses only f.v.
+// rescale).  bx: the lane's score maximum from tile_scores.  Uses only f.v.
+// (max(s) c is max(s c) exactly: rounding is monotone and c > 0.)
 template <int D>
-__device__ inline void tile_finish_full(RowTile<D>& rt, const Frags<D>& f, const float (&x)[8]) {
-    lazy_rescale<D>(rt, max_lane_groups(max8(x)));
-    accumulate<D>(rt, f, x, rt.m);
+__device__ inline void tile_finish_full(RowTile<D>& rt, const Frags<D>& f, const float (&x)[8], float bx,
+                                        float c) {
+    lazy_rescale<D>(rt, max_lane_groups(bx) * c);
+    accumulate<D>(rt, f, x, c, rt.m);
 }
 
 // tile_finish_full for all row tiles of a wave at once: one rescale test for
@@ -191,12 +198,13 @@ __device__ inline void tile_finish_full(RowTile<D>& rt, const Frags<D>& f, const
 // block, so the products of one row tile can run beside the exponentials of
 // the next.
 template <int D, int RT>
-__device__ inline void tiles_finish_full(RowTile<D> (&rt)[RT], const Frags<D>& f, const float (&x)[RT][8]) {
+__device__ inline void tiles_finish_full(RowTile<D> (&rt)[RT], const Frags<D>& f, const float (&x)[RT][8],
+                                         const float (&bx)[RT], float c) {
     float bm[RT];
     bool up[RT], any = false;
 #pragma unroll
     for (int tr = 0; tr < RT; ++tr) {
-        bm[tr] = max_lane_groups(max8(x[tr]));
+        bm[tr] = max_lane_groups(bx[tr]) * c;
         up[tr] = bm[tr] - rt[tr].m > kLazyLog2;
         any = any || up[tr];
     }
@@ -215,18 +223,22 @@ __device__ inline void tiles_finish_full(RowTile<D> (&rt)[RT], const Frags<D>& f
         }
     }
 #pragma unroll
-    for (int tr = 0; tr < RT; ++tr) accumulate<D>(rt[tr], f, x[tr], rt[tr].m);
+    for (int tr = 0; tr < RT; ++tr) accumulate<D>(rt[tr], f, x[tr], c, rt[tr].m);
 }
 
 // the rest of a tile with masks (invalid keys get -inf; a row-head that has
-// seen no valid key keeps m = -inf and takes p = 0); uses only f.v
+// seen no valid key keeps m = -inf and takes p = 0); uses only f.v.  The
+// maximum of the valid scores is at most bx, the maximum of all eight; taking
+// the smaller of the two keeps bx in use on this path too, so its computation
+// stays where tile_scores put it (fminf: an invalid key's score may be NaN,
+// and then bx is too).
 template <int D>
 __device__ inline void tile_finish_masked(RowTile<D>& rt, const Frags<D>& f, float (&x)[8],
-                                          const bool (&valid)[8]) {
+                                          const bool (&valid)[8], float bx, float c) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = valid[e] ? x[e] : -INFINITY;
-    lazy_rescale<D>(rt, max_lane_groups(max8(x)));
-    accumulate<D>(rt, f, x, rt.m == -INFINITY ? 0.f : rt.m);   // finite reference
+    lazy_rescale<D>(rt, max_lane_groups(fminf(max8(x), bx)) * c);
+    accumulate<D>(rt, f, x, c, rt.m == -INFINITY ? 0.f : rt.m);   // finite reference
 }
 
 // One key tile against one row tile.  `full`: every key of the tile is valid
@@ -235,13 +247,14 @@ template <int D>
 __device__ inline void tile_update(RowTile<D>& rt, const Frags<D>& f, bool full,
                                    const bool (&valid)[8], float c) {
     float x[8];
-    tile_scores<D>(rt, f, x, c);
+    float bx = tile_scores<D>(rt, f, x);
     if (!full) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = valid[e] ? x[e] : -INFINITY;
+        bx = fminf(max8(x), bx);
     }
-    lazy_rescale<D>(rt, max_lane_groups(max8(x)));
-    accumulate<D>(rt, f, x, rt.m == -INFINITY ? 0.f : rt.m);   // finite reference
+    lazy_rescale<D>(rt, max_lane_groups(bx) * c);
+    accumulate<D>(rt, f, x, c, rt.m == -INFINITY ? 0.f : rt.m);   // finite reference
 }
 
 // ---------------------------------------------------------------- item// ---------------------------------------------------------------- item
@@ -1073,11 +1086,11 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
     // fast phase: every row-head reads both tiles of the iteration in full
     for (; j < n_fast; ++j) {
         advance(j);
-        float x[RTW][8];
+        float x[RTW][8], bx[RTW];
 #pragma unroll
-        for (int tr = 0; tr < RTW; ++tr) tile_scores<D>(rt[tr], f, x[tr], sl2);
+        for (int tr = 0; tr < RTW; ++tr) bx[tr] = tile_scores<D>(rt[tr], f, x[tr]);
         next_keys(j);
-        tiles_finish_full<D, RTW>(rt, f, x);
+        tiles_finish_full<D, RTW>(rt, f, x, bx, sl2);
         next_values(j);
     }
     // general phase: deep tiles with masks, then ring tiles
@@ -1113,14 +1126,15 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
 #pragma unroll
             for (int tr = 0; tr < RTW; ++tr) mode[tr] = 0;
         }
+        float bx[RTW];
 #pragma unroll
         for (int tr = 0; tr < RTW; ++tr)
-            if (mode[tr]) tile_scores<D>(rt[tr], f, x[tr], sl2);
+            if (mode[tr]) bx[tr] = tile_scores<D>(rt[tr], f, x[tr]);
         next_keys(j);
 #pragma unroll
         for (int tr = 0; tr < RTW; ++tr) {
-            if (mode[tr] == 2) tile_finish_full<D>(rt[tr], f, x[tr]);
-            else if (mode[tr] == 1) tile_finish_masked<D>(rt[tr], f, x[tr], v[tr]);
+            if (mode[tr] == 2) tile_finish_full<D>(rt[tr], f, x[tr], bx[tr], sl2);
+            else if (mode[tr] == 1) tile_finish_masked<D>(rt[tr], f, x[tr], v[tr], bx[tr], sl2);
         }
         next_values(j);
     }
