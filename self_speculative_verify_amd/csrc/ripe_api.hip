@@ -92,6 +92,7 @@ bool view_ok(const ripe_kv_view& v) {
 struct Plan {
     bool rows_kernel;
     bool priv;         // rows kernel with private waves for the ring and block tiles
+    bool wide;         // keys kernel with eight waves
     int rt, nrb, nc, n_groups, M;
     int64_t cl, cx;
     size_t ws_bytes;
@@ -140,6 +141,7 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
     const int force_kernel = env_int("RIPE_KERNEL", 0);
     const int force_min_chunk = env_int("RIPE_MIN_CHUNK", 0);
     const int force_priv = env_int("RIPE_PRIV", 0);      // 1 off, 2 on
+    const int force_waves = env_int("RIPE_KEYS_WAVES", 0);  // 4 or 8
     Plan p;
     p.M = rows_here * (g.Hq / g.Hkv);
     // the rows kernel pays off once a KV head carries a hundred row-heads or more
@@ -169,9 +171,18 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
     // workgroup target: one round of the rows kernel; for the keys kernel
     // (two workgroups per CU) a second round only pays off on long contexts,
     // where the chunks stay long enough to outweigh the extra partial states
-    const int64_t slots = draft ? 0 : target_env ? target_env
-                                    : (p.rows_kernel || lmax <= 4096 ? 256 : 512);
     const int64_t cx = 32 * extra_tiles(g, rows, rows_here, p.M, p.nrb, rows_per_item, lmax);
+    // Keys kernel items of at most 16 tiles (two per wave of eight) are read
+    // unsplit by one eight-wave workgroup: no partial states and no combine
+    // launch, which on such short items costs more than the split saves
+    // (2-head, 128-position calls: 15.5 against 18.8 us).  Longer items split
+    // (a Huginn-scale per-loop call, 35 tiles: 15.8 us split, 16.7 unsplit
+    // with eight waves, 17.3 with four).
+    const bool auto_wide = !p.rows_kernel && !draft && !force_waves && !target_env &&
+                           (lmax + 31) / 32 + cx / 32 <= 16;
+    p.wide = !p.rows_kernel && !draft && (force_waves ? force_waves == 8 : auto_wide);
+    const int64_t slots = draft || auto_wide ? 0 : target_env ? target_env
+                                    : (p.rows_kernel || lmax <= 4096 ? 256 : 512);
     const int64_t min_chunk = force_min_chunk ? force_min_chunk : std::max<int64_t>(256, 8 * rows_per_item);
     // One chunk length for every sequence, from their total: the pairs that
     // fit one round of slots share the work evenly however ragged the
@@ -407,7 +418,7 @@ ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32
         for (int b = 0; b < ripe::kMaxSeqArgs; ++b)
             a.snc[b] = b < g.B ? (lens[b] > 0 ? (int32_t)((lens[b] + p.cx + p.cl - 1) / p.cl) : 1) : 0;
         const hipError_t e = p.rows_kernel ? ripe::launch_verify_rows(a, p.rt, p.priv, stream)
-                                           : ripe::launch_verify_keys(a, p.rt, stream);
+                                           : ripe::launch_verify_keys(a, p.rt, p.wide, stream);
         if (e != hipSuccess) return RIPE_EDEVICE;
         if (p.nc > 1 && ripe::launch_combine(a, stream) != hipSuccess) return RIPE_EDEVICE;
     }

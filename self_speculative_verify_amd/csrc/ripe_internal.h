@@ -114,7 +114,9 @@ struct VerifyArgs {
 // and "rows" (each wave owns 16*rt row-heads; the workgroup 64*rt)
 int keys_max_row_tiles(int d);
 int rows_max_row_tiles(int d);
-hipError_t launch_verify_keys(const VerifyArgs& a, int rt, hipStream_t s);
+// wide: eight waves instead of four (one workgroup per compute unit; not for
+// the windowed draft)
+hipError_t launch_verify_keys(const VerifyArgs& a, int rt, bool wide, hipStream_t s);
 // priv: four more waves take the ring and draft-block tiles (where rows_private_waves)
 bool rows_private_waves(int d, int rt);
 hipError_t launch_verify_rows(const VerifyArgs& a, int rt, bool priv, hipStream_t s);

@@ -27,9 +27,9 @@
 //                   global->LDS loads and read by all four waves; ring and
 //                   block tiles, which only the waves holding that loop need,
 //                   are loaded by those waves alone.
-//   k_verify_keys - few row-heads (a wave, or a small grid).  The four waves
-//                   hold the same row-heads, split the key tiles between them
-//                   and merge their softmax states through LDS.
+//   k_verify_keys - few row-heads (a wave, or a small grid).  The four (or
+//                   eight) waves hold the same row-heads, split the key tiles
+//                   between them and merge their softmax states through LDS.
 // A single-chunk item writes O and LSE; otherwise each chunk writes its
 // partial state (m, l, O) and k_combine merges them.
 #include "ripe_internal.h"
@@ -1285,14 +1285,17 @@ struct Job {
     const uint16_t* V;
 };
 
-// WIN: windowed draft attention (sinks and a window of committed keys)
-template <int D, int RT, bool WIN>
-__global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
-    constexpr int kStage = 4 * 2 * 32 * D;             // uint16: per-wave block tiles
-    constexpr int kMerge = 2 * RT * 16 * (D + 2);      // floats: merge buffers
+// WIN: windowed draft attention (sinks and a window of committed keys).
+// NW waves (4, two workgroups per compute unit, or 8, one): eight halve the
+// tiles each wave reads in turn, for items that one workgroup reads unsplit.
+template <int D, int RT, bool WIN, int NW>
+__global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) k_verify_keys(VerifyArgs a) {
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
+    constexpr int kStage = NW * 2 * 32 * D;            // uint16: per-wave block tiles
+    constexpr int kMerge = NW / 2 * RT * 16 * (D + 2); // floats: merge buffers
     constexpr int kLds = (kStage * 2 > kMerge * 4) ? kStage * 2 : kMerge * 4;
     __shared__ __attribute__((aligned(16))) unsigned char s_raw[kLds];
-    __shared__ int s_lw[4][64];                        // per wave: loop list
+    __shared__ int s_lw[NW][64];                       // per wave: loop list
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -1431,13 +1434,13 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
         init_row_word<D>(a, it, u, __shfl(w0, u < a.M ? u / G - k_lo : 0), q, rt[t]);
     }
 
-    for (int j = wave; j < n_jobs; j += 4) {
+    for (int j = wave; j < n_jobs; j += NW) {
         const Job jb = job_of(j);
         const int kind = __builtin_amdgcn_readfirstlane(jb.kind);
         const int jr = __builtin_amdgcn_readfirstlane(jb.r);
         const int base = __builtin_amdgcn_readfirstlane(jb.base);
         Frags<D> fn;
-        if (kAhead) comm_load(j + 4, fn);
+        if (kAhead) comm_load(j + NW, fn);
         else if (kind != 2 && j != wave) comm_load(j, f);
         if (kind == 2) {
             stage_block<D>(a, jb.K, jb.V, base, sk, sv, lane);
@@ -1458,7 +1461,7 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
         if (kAhead) f = fn;
     }
 
-    // merge the four waves' states: (2,3) -> (0,1) -> 0
+    // merge the waves' states pairwise: (NW/2 .. NW-1) -> (0 .. NW/2-1) -> .. -> 0
 #pragma unroll
     for (int tr = 0; tr < RT; ++tr) sum_lane_groups<D>(rt[tr]);
     auto put = [&](int buf) {
@@ -1491,10 +1494,13 @@ __global__ void __launch_bounds__(256, 2) k_verify_keys(VerifyArgs a) {
         }
     };
     __syncthreads();            // every wave is done with its staging tile
-    if (wave >= 2) put(wave - 2);
-    __syncthreads();
-    if (wave < 2) take(wave);
-    __syncthreads();
+#pragma unroll
+    for (int half = NW / 2; half > 1; half /= 2) {
+        if (wave >= half && wave < 2 * half) put(wave - half);
+        __syncthreads();
+        if (wave < half) take(wave);
+        __syncthreads();
+    }
     if (wave == 1) put(0);
     __syncthreads();
     if (wave != 0) return;
@@ -1623,20 +1629,31 @@ hipError_t launch_items(K kern, const VerifyArgs& a, hipStream_t s, int threads 
 int keys_max_row_tiles(int d) { return d == 128 ? 1 : 2; }
 int rows_max_row_tiles(int d) { return d == 96 ? 1 : 2; }
 
-hipError_t launch_verify_keys(const VerifyArgs& a, int rt, hipStream_t s) {
+hipError_t launch_verify_keys(const VerifyArgs& a, int rt, bool wide, hipStream_t s) {
     if (rt < 1 || rt > keys_max_row_tiles(a.d)) return hipErrorInvalidValue;
     const bool win = a.w_draft >= 0;
+    if (wide && win) return hipErrorInvalidValue;
+    if (wide) {
+        switch (a.d * 4 + rt) {
+            case 64 * 4 + 1: return launch_items(k_verify_keys<64, 1, false, 8>, a, s, 512);
+            case 64 * 4 + 2: return launch_items(k_verify_keys<64, 2, false, 8>, a, s, 512);
+            case 96 * 4 + 1: return launch_items(k_verify_keys<96, 1, false, 8>, a, s, 512);
+            case 96 * 4 + 2: return launch_items(k_verify_keys<96, 2, false, 8>, a, s, 512);
+            case 128 * 4 + 1: return launch_items(k_verify_keys<128, 1, false, 8>, a, s, 512);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (a.d * 8 + rt * 2 + (win ? 1 : 0)) {
-        case 64 * 8 + 2: return launch_items(k_verify_keys<64, 1, false>, a, s);
-        case 64 * 8 + 4: return launch_items(k_verify_keys<64, 2, false>, a, s);
-        case 96 * 8 + 2: return launch_items(k_verify_keys<96, 1, false>, a, s);
-        case 96 * 8 + 4: return launch_items(k_verify_keys<96, 2, false>, a, s);
-        case 128 * 8 + 2: return launch_items(k_verify_keys<128, 1, false>, a, s);
-        case 64 * 8 + 3: return launch_items(k_verify_keys<64, 1, true>, a, s);
-        case 64 * 8 + 5: return launch_items(k_verify_keys<64, 2, true>, a, s);
-        case 96 * 8 + 3: return launch_items(k_verify_keys<96, 1, true>, a, s);
-        case 96 * 8 + 5: return launch_items(k_verify_keys<96, 2, true>, a, s);
-        case 128 * 8 + 3: return launch_items(k_verify_keys<128, 1, true>, a, s);
+        case 64 * 8 + 2: return launch_items(k_verify_keys<64, 1, false, 4>, a, s);
+        case 64 * 8 + 4: return launch_items(k_verify_keys<64, 2, false, 4>, a, s);
+        case 96 * 8 + 2: return launch_items(k_verify_keys<96, 1, false, 4>, a, s);
+        case 96 * 8 + 4: return launch_items(k_verify_keys<96, 2, false, 4>, a, s);
+        case 128 * 8 + 2: return launch_items(k_verify_keys<128, 1, false, 4>, a, s);
+        case 64 * 8 + 3: return launch_items(k_verify_keys<64, 1, true, 4>, a, s);
+        case 64 * 8 + 5: return launch_items(k_verify_keys<64, 2, true, 4>, a, s);
+        case 96 * 8 + 3: return launch_items(k_verify_keys<96, 1, true, 4>, a, s);
+        case 96 * 8 + 5: return launch_items(k_verify_keys<96, 2, true, 4>, a, s);
+        case 128 * 8 + 3: return launch_items(k_verify_keys<128, 1, true, 4>, a, s);
     }
     return hipErrorInvalidValue;
 }

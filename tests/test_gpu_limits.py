@@ -26,10 +26,14 @@ def _gpu():
     yield
 
 
-@pytest.fixture(params=["auto", "keys", "rows", "keys-chunked"], autouse=True)
+@pytest.fixture(params=["auto", "keys", "keys-8waves", "rows", "keys-chunked"], autouse=True)
 def kernel_choice(request, monkeypatch):
-    if request.param in ("keys", "keys-chunked"):
+    if request.param in ("keys", "keys-8waves", "keys-chunked"):
         monkeypatch.setenv("RIPE_KERNEL", "1")
+    if request.param == "keys":
+        monkeypatch.setenv("RIPE_KEYS_WAVES", "4")
+    if request.param == "keys-8waves":
+        monkeypatch.setenv("RIPE_KEYS_WAVES", "8")
     if request.param == "rows":
         monkeypatch.setenv("RIPE_KERNEL", "2")
     if request.param == "keys-chunked":
