@@ -172,14 +172,14 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
     // (two workgroups per CU) a second round only pays off on long contexts,
     // where the chunks stay long enough to outweigh the extra partial states
     const int64_t cx = 32 * extra_tiles(g, rows, rows_here, p.M, p.nrb, rows_per_item, lmax);
-    // Keys kernel items of at most 16 tiles (two per wave of eight) are read
+    // Keys kernel items of at most 32 tiles (four per wave of eight) are read
     // unsplit by one eight-wave workgroup: no partial states and no combine
-    // launch, which on such short items costs more than the split saves
-    // (2-head, 128-position calls: 15.5 against 18.8 us).  Longer items split
-    // (a Huginn-scale per-loop call, 35 tiles: 15.8 us split, 16.7 unsplit
-    // with eight waves, 17.3 with four).
+    // launch, which on such short items costs more than the split saves (a
+    // 2-head, 128-position call of 19-tile items: 15.5 against 18.8 us).
+    // Longer items split (a Huginn-scale per-loop call, 35 tiles: 15.8 us
+    // split, 16.7 unsplit with eight waves, 17.3 with four).
     const bool auto_wide = !p.rows_kernel && !draft && !force_waves && !target_env &&
-                           (lmax + 31) / 32 + cx / 32 <= 16;
+                           (lmax + 31) / 32 + cx / 32 <= 32;
     p.wide = !p.rows_kernel && !draft && (force_waves ? force_waves == 8 : auto_wide);
     const int64_t slots = draft || auto_wide ? 0 : target_env ? target_env
                                     : (p.rows_kernel || lmax <= 4096 ? 256 : 512);
