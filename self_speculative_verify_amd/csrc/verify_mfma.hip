@@ -689,34 +689,41 @@ __device__ __attribute__((always_inline)) inline void private_wave(const VerifyA
     // every deep load is done and every wave has left the stages
     lds_barrier();
     if (it.last && pf_ok) {
-        uint16_t* sk = stages + rw * 2 * TILE;
-        uint16_t* sv = sk + TILE;
+        // The prefetched rows go row-major into the wave's part of the stages
+        // ([kv][key][dim], 16-byte writes), and the operands are read from
+        // there: a key operand is key n's 16 bytes at dims 32c + 8q (keys 8 and
+        // up, and the second key half, are zero); a value operand holds keys
+        // 4q..4q+3 at dim 16dt + n in its first four columns (lane groups 0
+        // and 1; its other columns are keys of 16 or more, zero).  Keys past
+        // the block were prefetched as zero, so nothing needs clearing.
+        uint16_t* rm = stages + rw * 2 * TILE;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             if (p >= nloops) break;
-            for (int z = lane; z < 2 * TILE / 8; z += 64)
-                *reinterpret_cast<uint4*>(sk + z * 8) = make_uint4(0, 0, 0, 0);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int k = 0; k < PB; ++k) {
                 const int pc = lane + 64 * k;
-                const int c8 = pc % (D / 8), rest = pc / (D / 8);
-                const int key = rest % 8, kv = rest / 8;
-                if (kv == 0) {
-                    *reinterpret_cast<uint4*>(sk + key_off(key, c8 * 8, D)) = pfb[p][k];
-                } else {
-                    const uint32_t w[4] = {pfb[p][k].x, pfb[p][k].y, pfb[p][k].z, pfb[p][k].w};
-#pragma unroll
-                    for (int cc = 0; cc < 8; ++cc)
-                        sv[val_off(key, c8 * 8 + cc, D)] = (uint16_t)(w[cc >> 1] >> (16 * (cc & 1)));
-                }
+                const int c8 = pc % (D / 8), rest = pc / (D / 8);   // rest = kv*8 + key
+                *reinterpret_cast<uint4*>(rm + rest * D + c8 * 8) = pfb[p][k];
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             Frags<D> f;
-            load_frags<D>(sk, sv, f, n, q);
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c) {
+                f.k[c][0] = n < 8 ? *reinterpret_cast<const uint4*>(rm + n * D + 32 * c + 8 * q)
+                                  : make_uint4(0, 0, 0, 0);
+                f.k[c][1] = make_uint4(0, 0, 0, 0);
+            }
+            const uint16_t* vr = rm + (8 + 4 * (q & 1)) * D;    // value rows of keys 4q..
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                const uint32_t v0 = vr[16 * dt + n], v1 = vr[D + 16 * dt + n];
+                const uint32_t v2 = vr[2 * D + 16 * dt + n], v3 = vr[3 * D + 16 * dt + n];
+                f.v[dt] = q < 2 ? make_uint4(v0 | (v1 << 16), v2 | (v3 << 16), 0, 0) : make_uint4(0, 0, 0, 0);
+            }
+            // every lane has read the rows before the next loop's overwrite them
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int tr = 0; tr < RTW; ++tr) {
