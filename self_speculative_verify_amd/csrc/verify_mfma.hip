@@ -378,6 +378,11 @@ __device__ inline void stage_block(const VerifyArgs& a, const uint16_t* K, const
     constexpr int NI = 32 * PK / 64;          // pieces per lane
     constexpr int GP = 2;                     // pieces loaded before any is stored
     const int n_keys = a.n_blk - base;        // keys of this tile inside the block
+    // the value tile is cleared with 16-byte stores and only the keys of the
+    // block are scattered into it: its 2-byte stores land in few LDS banks
+#pragma unroll
+    for (int z = 0; z < D / 16; ++z)
+        *reinterpret_cast<uint4*>(sv + (z * 64 + lane) * 8) = make_uint4(0, 0, 0, 0);
 #pragma unroll 1
     for (int t0 = 0; t0 < NI; t0 += GP) {
         uint4 kx[GP], vx[GP];
@@ -398,10 +403,12 @@ __device__ inline void stage_block(const VerifyArgs& a, const uint16_t* K, const
             const int it = lane + 64 * (t0 + u);
             const int key = it / PK, e0 = (it % PK) * 8;
             *reinterpret_cast<uint4*>(sk + key_off(key, e0, D)) = kx[u];
-            const uint32_t w[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
+            if (key < n_keys) {
+                const uint32_t w[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
 #pragma unroll
-            for (int cc = 0; cc < 8; ++cc)
-                sv[val_off(key, e0 + cc, D)] = (uint16_t)(w[cc >> 1] >> (16 * (cc & 1)));
+                for (int cc = 0; cc < 8; ++cc)
+                    sv[val_off(key, e0 + cc, D)] = (uint16_t)(w[cc >> 1] >> (16 * (cc & 1)));
+            }
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
