@@ -21,12 +21,17 @@
 // values transposed, in exactly the operand order of the instruction.
 //
 // Two kernels share that tile step:
-//   k_verify_rows - many row-heads per KV head (the D x R grid).  Each wave
-//                   owns 16*RTW row-heads; the deep tiles are staged once per
-//                   workgroup through a 4-stage LDS pipeline fed by direct
-//                   global->LDS loads and read by all four waves; ring and
-//                   block tiles, which only the waves holding that loop need,
-//                   are loaded by those waves alone.
+//   k_verify_rows - many row-heads per KV head (the D x R grid).  Eight
+//                   waves: four row groups of 16*RTW row-heads, each split
+//                   into two key halves (even and odd tiles).  The tile stream
+//                   is staged once per workgroup through a 5-, 6- or 10-stage
+//                   LDS pipeline (head_dim 128, 96, 64) fed by direct
+//                   global->LDS loads from all eight waves.  With private
+//                   waves (four more, one per row group) the ring and block
+//                   tiles, which only that row group's loops read, go from
+//                   memory into the private wave's registers beside the deep
+//                   stream; without them the ring tiles follow the deep tiles
+//                   in the stream and the block tiles come after the loop.
 //   k_verify_keys - few row-heads (a wave, or a small grid).  The four (or
 //                   eight) waves hold the same row-heads, split the key tiles
 //                   between them and merge their softmax states through LDS.
