@@ -84,9 +84,10 @@ bool view_ok(const ripe_kv_view& v) {
 // whole workgroup 16*rt and splits the key tiles between its waves.
 // Committed positions split into chunks of cl (a multiple of 32) when the row
 // blocks alone leave workgroup slots of the chip empty (one rows workgroup or
-// two keys workgroups fit on a compute unit); the count stops at one round of
-// slots, so no workgroup waits for another to finish, and at chunks long
-// enough that their partial states cost little next to the keys they read.
+// two four-wave keys workgroups fit on a compute unit); the count stops at one
+// round of slots, so no workgroup waits for another to finish, and at chunks
+// long enough that their partial states cost little next to the keys they
+// read.  Short keys items instead go unsplit to an eight-wave workgroup.
 // The last chunk of a sequence also takes the ring and draft-block tiles of
 // its row block, so it reads cx fewer committed positions than the others.
 struct Plan {
