@@ -139,15 +139,49 @@ int32_t ripe_max_batch(const ripe_config* cfg, size_t budget_bytes);
 /*
  * Bind a handle to caller-owned storage of at least ripe_cache_bytes(cfg)
  * bytes (device memory, 256-byte aligned) and zero-fill it on `stream`.
- * All lengths start at 0.  The storage must outlive the handle.
+ * All lengths start at 0.  The storage must outlive the handle.  The handle
+ * is the host state of one RIPE cache (RIPE abstract, fourth sentence: what
+ * the cache stores); no page defines the call itself.
  */
 ripe_status ripe_cache_create(const ripe_config* cfg, void* d_storage, size_t bytes,
                               hipStream_t stream, ripe_cache** out);
 
-/* Release the handle (host memory only).  NULL is accepted. */
+/*
+ * Release the handle (host memory only; the storage stays the caller's).
+ * NULL is accepted, and so is a handle that was already destroyed: the
+ * library keeps a registry of live handles and ignores any other pointer (a
+ * later ripe_cache_create may reuse the address of a destroyed handle, so a
+ * destroyed handle must still not be passed to the other calls).  No page
+ * defines the call.
+ */
 void ripe_destroy(ripe_cache* cache);
 
-/* Host copy of the committed lengths of one layer (B values). */
+/*
+ * Fixed launch choices for one handle, for tuning sweeps and for tests that
+ * run every kernel variant on the same inputs; a zero field leaves that
+ * choice to the planner, and a NULL tuning restores the planner for all of
+ * them.  Results never depend on these choices beyond float rounding order.
+ * No page defines the call; the library reads no environment variable.
+ * RIPE_EINVAL for a dead handle or an out-of-range field (nothing changed).
+ */
+typedef struct {
+    int32_t kernel;        /* 1: keys kernel (waves split the key tiles),
+                              2: rows kernel (waves own row-heads) */
+    int32_t keys_waves;    /* 4 or 8 waves in a keys workgroup */
+    int32_t row_tiles;     /* 1 or 2 tiles of 16 row-heads per wave (clamped
+                              to what the head size allows) */
+    int32_t private_waves; /* rows kernel: 1 without, 2 with the private waves
+                              for ring and block tiles (head sizes 64, 96) */
+    int32_t items_target;  /* workgroups the split of committed positions aims
+                              for (1: never split) */
+    int32_t min_chunk;     /* shortest chunk of committed positions (rounded up
+                              to 32) */
+} ripe_tuning;
+
+ripe_status ripe_set_tuning(ripe_cache* cache, const ripe_tuning* tuning);
+
+/* Host copy of the committed lengths of one layer (B values); no page defines
+ * the call. */
 ripe_status ripe_get_lengths(const ripe_cache* cache, int32_t layer, int32_t* h_lens);
 
 /*
@@ -168,9 +202,14 @@ ripe_status ripe_append(ripe_cache* cache, int32_t layer, const int32_t* h_n_new
                         ripe_kv_view win_v, hipStream_t stream);
 
 /*
- * Workspace (device bytes) a ripe_verify_attn call with n_rows rows needs at
- * the handle's current lengths (partial softmax states of split key ranges);
- * may be 0.
+ * Workspace (device bytes) that any ripe_verify_attn call with n_rows rows
+ * needs at the handle's current lengths, on any layer and for any set of rows
+ * of that size (partial softmax states of split key ranges, for every launch
+ * of the call: calls of more than 256 rows run several); may be 0.  0 also
+ * for a dead handle or n_rows outside 1..65535.  Takes the handle rather than
+ * the configuration because the split depends on the current lengths; after
+ * an append the size must be queried again.  No page defines the call (the
+ * split of the key range is this library's).
  */
 size_t ripe_workspace_bytes(const ripe_cache* cache, int32_t n_rows);
 
@@ -185,6 +224,12 @@ size_t ripe_workspace_bytes(const ripe_cache* cache, int32_t n_rows);
  *   d_ws:  at least ripe_workspace_bytes(cache, n_rows) bytes (256-aligned),
  *          or NULL when that is 0.
  * Committed positions come from the storage at the handle's current lengths.
+ * Follows the RIPE abstract, first sentence (the draft block verified at
+ * every loop over the shared prefix) and fifth sentence (block keys against
+ * the window), and the WaveFront page's mixed-depth batched verification
+ * (rows at different loops in one call).  RIPE_EINVAL (nothing enqueued) for
+ * a dead handle, a layer, row, loop or n_blk out of range, a null or
+ * misaligned pointer, a bad view, or a workspace below the size above.
  */
 ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
                              const int32_t* h_row_blk, const int32_t* h_row_loop,

@@ -25,20 +25,25 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ripe_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libripe_oracle.so")
+# RIPE_ORACLE_LIB: load another build of ripe_oracle.c instead (the test
+# suite's sanitizer run points it at an instrumented build)
+_LIB_PATH = os.environ.get("RIPE_ORACLE_LIB") or os.path.join(_HERE, "libripe_oracle.so")
 _lib = None
 
 ORA_OK, ORA_EINVAL, ORA_ECAPACITY, ORA_EMISSING = 0, 1, 2, 4
 
 
-def build(force: bool = True) -> str:
-    """Compile the C oracle in place (gcc, -O2, OpenMP)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = f"{_LIB_PATH}.{os.getpid()}.tmp"
+def build(force: bool = True, out: Optional[str] = None, extra_flags: Sequence[str] = ()) -> str:
+    """Compile the C oracle (gcc, -O2, OpenMP), in place unless ``out`` names
+    another file (extra_flags: e.g. sanitizers)."""
+    path = out or _LIB_PATH
+    stale = not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC)
+    if force or stale:
+        tmp = f"{path}.{os.getpid()}.tmp"
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
-                               "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+                               *extra_flags, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, path)
+    return path
 
 
 class OraConfig(ctypes.Structure):
@@ -68,6 +73,8 @@ def lib():
                                 P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                 P, P, P]
         L.ora_threads.restype = ctypes.c_int32
+        L.ora_set_threads.restype = None
+        L.ora_set_threads.argtypes = [ctypes.c_int32]
         _lib = L
     return _lib
 
@@ -96,6 +103,11 @@ def layout_value(cfg: OraConfig, which: str) -> int:
 
 def threads() -> int:
     return int(lib().ora_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle uses from now on (OpenMP)."""
+    lib().ora_set_threads(int(n))
 
 
 class OracleCache:

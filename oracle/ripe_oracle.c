@@ -389,3 +389,13 @@ int32_t ora_threads(void) {
 #endif
     return n;
 }
+
+/* set the number of OpenMP threads later calls use (n >= 1; for the
+ * single-thread CPU baseline) */
+void ora_set_threads(int32_t n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -18,7 +18,9 @@ HIPCC_FLAGS = [
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    """Kernels (.hip) and host code (.cpp, plain C++ that hipcc compiles too)."""
+    csrc = os.path.join(PKG, "csrc")
+    return sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.cpp")))
 
 
 def build(verbose: bool = False) -> str:

@@ -10,6 +10,10 @@ import torch
 
 from . import ripe as _r
 
+# Launch choices applied to every cache created while it is set (a dict of
+# RipeTuning fields), for test fixtures that run every kernel variant.
+DEFAULT_TUNING: Optional[dict] = None
+
 
 class RipeCache:
     """Storage tensor + handle for one configuration.
@@ -21,7 +25,8 @@ class RipeCache:
 
     def __init__(self, n_layers: int, n_loops: int, n_heads_q: int, n_heads_kv: int,
                  head_dim: int, window: int, batch: int, capacity: int, max_block: int,
-                 anchor: int = _r.RIPE_ANCHOR_QUERY, device="cuda", stream=None):
+                 anchor: int = _r.RIPE_ANCHOR_QUERY, device="cuda", stream=None,
+                 tuning: Optional[dict] = None):
         self.cfg = _r.config(n_layers, n_loops, n_heads_q, n_heads_kv, head_dim, window, batch,
                              capacity, max_block, anchor)
         nbytes = _r.ripe_cache_bytes(self.cfg)
@@ -32,6 +37,9 @@ class RipeCache:
             raise RuntimeError("storage allocation is not 256-byte aligned")
         self.handle = _r.ripe_cache_create(self.cfg, self.storage, stream)
         self._ws = None
+        tuning = DEFAULT_TUNING if tuning is None else tuning
+        if tuning:
+            _r.ripe_set_tuning(self.handle, tuning)
 
     # ------------------------------------------------------------------
     @property

@@ -17,6 +17,7 @@
 #include <algorithm>
 
 #include "ripe_internal.h"
+#include "tile_layout.h"
 
 namespace ripe {
 namespace {

@@ -1,28 +1,31 @@
 // Host side of the RIPE C ABI: configuration checks, storage geometry, the
 // host copy of the committed lengths, and kernel launches on the caller's
 // stream.  See include/ripe.h for the contract of every entry point.
+//
+// Plain host C++ (HIP runtime API only): the test suite also compiles this
+// file with a host compiler and sanitizers, against recording stand-ins of
+// the kernel launchers, to check every validation path on the CPU.
 #include "ripe.h"
 #include "ripe_internal.h"
 
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <unordered_set>
 #include <vector>
 
 using ripe::Geometry;
 
 struct ripe_cache {
-    uint64_t magic;
     Geometry g;
     uint8_t* storage;
     std::vector<int32_t> lens;   // [n_layers][B], host copy of the lens section
+    ripe::Tuning tuning;         // all zero: the planner decides
 };
 
 namespace {
-
-constexpr uint64_t kMagic = 0x52495045434143ull;   // "RIPECAC"
 
 int64_t up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -64,7 +67,20 @@ Geometry geometry(const ripe_config* c) {
     return g;
 }
 
-bool live(const ripe_cache* c) { return c && c->magic == kMagic; }
+// Handles that ripe_cache_create returned and ripe_destroy has not released.
+// Every entry point looks its handle up here, so a handle that was already
+// destroyed (or never created) is refused instead of read.
+std::mutex g_handles_mu;
+std::unordered_set<const ripe_cache*>& handles() {
+    static std::unordered_set<const ripe_cache*> h;
+    return h;
+}
+
+bool live(const ripe_cache* c) {
+    if (!c) return false;
+    std::lock_guard<std::mutex> lock(g_handles_mu);
+    return handles().count(c) != 0;
+}
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -76,141 +92,6 @@ bool view_ok(const ripe_kv_view& v) {
     for (int64_t x : s)
         if (x < 0 || x % 8) return false;
     return true;
-}
-
-// How one launch covers a call.  Row-heads (query row x query head of a KV
-// group) of a KV head: with 128 or more the "rows" kernel gives each wave
-// 16*rt of them and a workgroup 64*rt; with fewer the "keys" kernel gives a
-// whole workgroup 16*rt and splits the key tiles between its waves.
-// Committed positions split into chunks of cl (a multiple of 32) when the row
-// blocks alone leave workgroup slots of the chip empty (one rows workgroup or
-// two four-wave keys workgroups fit on a compute unit); the count stops at one
-// round of slots, so no workgroup waits for another to finish, and at chunks
-// long enough that their partial states cost little next to the keys they
-// read.  Short keys items instead go unsplit to an eight-wave workgroup.
-// The last chunk of a sequence also takes the ring and draft-block tiles of
-// its row block, so it reads cx fewer committed positions than the others.
-struct Plan {
-    bool rows_kernel;
-    bool priv;         // rows kernel with private waves for the ring and block tiles
-    bool wide;         // keys kernel with eight waves
-    int rt, nrb, nc, n_groups, M;
-    int64_t cl, cx;
-    size_t ws_bytes;
-};
-
-int env_int(const char* name, int fallback) {
-    const char* e = std::getenv(name);
-    const int v = e ? std::atoi(e) : 0;
-    return v > 0 ? v : fallback;
-}
-
-// Tiles of the ring and draft-block work of the heaviest row block (rows:
-// sorted row words of the launch; null for a bound over every row set).
-int64_t extra_tiles(const Geometry& g, const uint32_t* rows, int rows_here, int M, int nrb,
-                    int rows_per_item, int64_t lmax) {
-    const int G = g.Hq / g.Hkv;
-    const int64_t ring_tiles = g.R > 1 ? (std::min<int64_t>(g.WR, lmax) + 31) / 32 : 0;
-    if (!rows) {
-        const int64_t nl = std::min<int64_t>(rows_per_item / G + 1, g.R);
-        return nl * ring_tiles + nl * ((g.max_block + 31) / 32);
-    }
-    int64_t most = 0;
-    for (int rb = 0; rb < nrb; ++rb) {
-        const int k_lo = rb * rows_per_item / G;
-        const int k_hi = std::min(rows_here, (std::min(M, (rb + 1) * rows_per_item) + G - 1) / G);
-        int64_t t = 0;
-        for (int k = k_lo; k < k_hi; ++k) {
-            const int r = (rows[k] >> 8) & 255, i = rows[k] & 255;
-            const bool first = k == k_lo || (int)((rows[k - 1] >> 8) & 255) != r;
-            const bool last = k + 1 == k_hi || (int)((rows[k + 1] >> 8) & 255) != r;
-            if (first && r < g.R) t += ring_tiles;
-            if (last) t += i / 32 + 1;     // rows of a loop are sorted by offset
-        }
-        most = std::max(most, t);
-    }
-    return most;
-}
-
-// draft: a windowed draft call (the keys kernel, one chunk: it reads only the
-// sinks and a short window, and needs no workspace)
-Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint32_t* rows,
-               bool draft = false) {
-    // tuning and test overrides: workgroup target, row tiles, kernel (1 keys, 2 rows)
-    const int target_env = env_int("RIPE_ITEMS_TARGET", 0);
-    const int force_rt = env_int("RIPE_ROW_TILES", 0);
-    const int force_kernel = env_int("RIPE_KERNEL", 0);
-    const int force_min_chunk = env_int("RIPE_MIN_CHUNK", 0);
-    const int force_priv = env_int("RIPE_PRIV", 0);      // 1 off, 2 on
-    const int force_waves = env_int("RIPE_KEYS_WAVES", 0);  // 4 or 8
-    Plan p;
-    p.M = rows_here * (g.Hq / g.Hkv);
-    // the rows kernel pays off once a KV head carries a hundred row-heads or more
-    p.rows_kernel = draft ? false : force_kernel ? force_kernel == 2 : p.M >= 128;
-    const int64_t heads = (int64_t)g.B * g.Hkv;
-    int rows_per_item;
-    if (p.rows_kernel) {
-        p.rt = ripe::rows_max_row_tiles(g.d);
-        if (p.rt > 1 && heads * ((p.M + 64 * p.rt - 1) / (64 * p.rt)) < 256) p.rt = 1;
-        rows_per_item = 64;
-    } else {
-        p.rt = std::min(p.M <= 16 ? 1 : 2, ripe::keys_max_row_tiles(g.d));
-        rows_per_item = 16;
-    }
-    if (force_rt > 0 && !draft) p.rt = std::min(force_rt, p.rows_kernel ? ripe::rows_max_row_tiles(g.d)
-                                                              : ripe::keys_max_row_tiles(g.d));
-    rows_per_item *= p.rt;
-    // private waves pay off when the row blocks have ring tiles to read
-    p.priv = p.rows_kernel && ripe::rows_private_waves(g.d, p.rt) &&
-             (force_priv ? force_priv == 2 : (g.R > 1 && g.WR > 0));
-    p.nrb = (p.M + rows_per_item - 1) / rows_per_item;
-    int64_t lmax = 0;
-    for (int b = 0; b < g.B; ++b) lmax = std::max<int64_t>(lmax, lens[b]);
-    // workgroups of one (sequence, chunk) pair, and of the whole call unsplit
-    const int64_t units = (int64_t)g.Hkv * p.nrb;
-    const int64_t base = g.B * units;
-    // workgroup target: one round of the rows kernel; for the keys kernel
-    // (two workgroups per CU) a second round only pays off on long contexts,
-    // where the chunks stay long enough to outweigh the extra partial states
-    const int64_t cx = 32 * extra_tiles(g, rows, rows_here, p.M, p.nrb, rows_per_item, lmax);
-    // Keys kernel items of at most 32 tiles (four per wave of eight) are read
-    // unsplit by one eight-wave workgroup: no partial states and no combine
-    // launch, which on such short items costs more than the split saves (a
-    // 2-head, 128-position call of 19-tile items: 15.5 against 18.8 us).
-    // Longer items split (a Huginn-scale per-loop call, 35 tiles: 15.8 us
-    // split, 16.7 unsplit with eight waves, 17.3 with four).
-    const bool auto_wide = !p.rows_kernel && !draft && !force_waves && !target_env &&
-                           (lmax + 31) / 32 + cx / 32 <= 32;
-    p.wide = !p.rows_kernel && !draft && (force_waves ? force_waves == 8 : auto_wide);
-    const int64_t slots = draft || auto_wide ? 0 : target_env ? target_env
-                                    : (p.rows_kernel || lmax <= 4096 ? 256 : 512);
-    const int64_t min_chunk = force_min_chunk ? force_min_chunk : std::max<int64_t>(256, 8 * rows_per_item);
-    // One chunk length for every sequence, from their total: the pairs that
-    // fit one round of slots share the work evenly however ragged the
-    // lengths are (a sequence gets ceil((L + cx) / cl) chunks).
-    int64_t cl = 0, nc_cap = 1;
-    if (base < slots) {
-        int64_t sum = 0;
-        for (int b = 0; b < g.B; ++b) sum += lens[b] > 0 ? lens[b] + cx : 0;
-        const int64_t pairs = slots / units;
-        cl = std::max<int64_t>(min_chunk, up((sum + pairs - 1) / std::max<int64_t>(pairs, 1), 32));
-        // a bound on the chunk count that never falls as rows or lengths grow
-        nc_cap = std::max<int64_t>(1, std::min<int64_t>(pairs, (lmax + cx + min_chunk - 1) / min_chunk));
-    }
-    if (cl == 0 || cl >= lmax + cx) {
-        p.cx = 0;
-        p.cl = std::max<int64_t>(32, up(lmax, 32));
-        p.nc = 1;
-    } else {
-        p.cx = cx;
-        p.cl = cl;
-        p.nc = (int)((lmax + cx + cl - 1) / cl);
-    }
-    p.n_groups = (int)(heads * p.nc);
-    // whenever a split is possible, so a size queried for a row count holds
-    // for every row set of that size
-    p.ws_bytes = base < slots ? (size_t)heads * nc_cap * p.M * (g.d + 2) * sizeof(float) : 0;
-    return p;
 }
 
 ripe::View as_view(const ripe_kv_view& v) {
@@ -265,23 +146,51 @@ ripe_status ripe_cache_create(const ripe_config* cfg, void* d_storage, size_t by
     if (bytes < (size_t)g.total) return RIPE_EINVAL;
     ripe_cache* c = new (std::nothrow) ripe_cache;
     if (!c) return RIPE_EDEVICE;
-    c->magic = kMagic;
     c->g = g;
     c->storage = static_cast<uint8_t*>(d_storage);
     c->lens.assign((size_t)g.n_layers * g.B, 0);
+    std::memset(&c->tuning, 0, sizeof(c->tuning));
     if (hipMemsetAsync(d_storage, 0, (size_t)g.total, stream) != hipSuccess) {
-        c->magic = 0;
         delete c;
         return RIPE_EDEVICE;
+    }
+    {
+        std::lock_guard<std::mutex> lock(g_handles_mu);
+        handles().insert(c);
     }
     *out = c;
     return RIPE_OK;
 }
 
 void ripe_destroy(ripe_cache* cache) {
-    if (!live(cache)) return;
-    cache->magic = 0;
+    if (!cache) return;
+    {
+        std::lock_guard<std::mutex> lock(g_handles_mu);
+        if (handles().erase(cache) == 0) return;   // not a live handle: nothing to release
+    }
     delete cache;
+}
+
+ripe_status ripe_set_tuning(ripe_cache* cache, const ripe_tuning* t) {
+    if (!live(cache)) return RIPE_EINVAL;
+    ripe::Tuning n;
+    std::memset(&n, 0, sizeof(n));
+    if (t) {
+        if (t->kernel < 0 || t->kernel > 2) return RIPE_EINVAL;
+        if (t->keys_waves != 0 && t->keys_waves != 4 && t->keys_waves != 8) return RIPE_EINVAL;
+        if (t->row_tiles < 0 || t->row_tiles > 2) return RIPE_EINVAL;
+        if (t->private_waves < 0 || t->private_waves > 2) return RIPE_EINVAL;
+        if (t->items_target < 0 || t->items_target > (1 << 24)) return RIPE_EINVAL;
+        if (t->min_chunk < 0 || t->min_chunk > (1 << 24)) return RIPE_EINVAL;
+        n.kernel = t->kernel;
+        n.keys_waves = t->keys_waves;
+        n.row_tiles = t->row_tiles;
+        n.private_waves = t->private_waves;
+        n.items_target = t->items_target;
+        n.min_chunk = t->min_chunk;
+    }
+    cache->tuning = n;
+    return RIPE_OK;
 }
 
 ripe_status ripe_get_lengths(const ripe_cache* cache, int32_t layer, int32_t* h_lens) {
@@ -346,26 +255,24 @@ ripe_status ripe_append(ripe_cache* cache, int32_t layer, const int32_t* h_n_new
 }
 
 size_t ripe_workspace_bytes(const ripe_cache* cache, int32_t n_rows) {
-    if (!live(cache) || n_rows <= 0) return 0;
-    const Geometry& g = cache->g;
-    const int32_t* lens = cache->lens.data();
-    size_t ws = 0;
-    for (int layer = 0; layer < g.n_layers; ++layer) {   // any layer may be verified
-        const int rows_here = std::min(ripe::kMaxRowsPerLaunch, (int)n_rows);
-        ws = std::max(ws, make_plan(g, lens + (size_t)layer * g.B, rows_here, nullptr).ws_bytes);
-    }
-    return ws;
+    if (!live(cache) || n_rows <= 0 || n_rows > 65535) return 0;
+    return ripe::workspace_bound(cache->g, cache->lens.data(), n_rows, cache->tuning);
 }
 
 }  // extern "C"
 
-namespace {
+namespace ripe {
 
-// ripe_verify_attn (n_sink = 0, w_draft = -1) and ripe_draft_attn
+// ripe_verify_attn (n_sink = 0, w_draft = -1) and ripe_draft_attn.  ws_fixed:
+// d_ws is a buffer of ws_bytes bytes that is refused only when one of the
+// call's launches needs more than that; otherwise the caller's workspace must
+// hold at least ripe_workspace_bytes for this row count.  Every argument and
+// every launch's partial-state size is checked before the first launch.
 ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32_t* h_row_blk,
                    const int32_t* h_row_loop, const void* d_q, ripe_kv_view blk_k,
                    ripe_kv_view blk_v, int32_t n_blk, int32_t n_sink, int32_t w_draft,
-                   float* d_out, float* d_lse, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+                   float* d_out, float* d_lse, void* d_ws, size_t ws_bytes, bool ws_fixed,
+                   hipStream_t stream) {
     const bool draft = w_draft >= 0;
     if (!live(cache) || layer < 0 || layer >= cache->g.n_layers) return RIPE_EINVAL;
     const Geometry& g = cache->g;
@@ -379,8 +286,10 @@ ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32
         if (h_row_blk[k] < 0 || h_row_blk[k] >= n_blk) return RIPE_EINVAL;
         if (h_row_loop[k] < 1 || h_row_loop[k] > g.R) return RIPE_EINVAL;
     }
-    const size_t need = draft ? 0 : ripe_workspace_bytes(cache, n_rows);
-    if (ws_bytes < need || (need > 0 && (!d_ws || !aligned(d_ws, 256)))) return RIPE_EINVAL;
+    if (!ws_fixed && !draft) {
+        const size_t bound = ripe_workspace_bytes(cache, n_rows);
+        if (ws_bytes < bound || (bound > 0 && (!d_ws || !aligned(d_ws, 256)))) return RIPE_EINVAL;
+    }
 
     // rows sorted by (loop, block offset) so that rows reading the same planes
     // are adjacent
@@ -390,7 +299,21 @@ ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32
     std::stable_sort(rows.begin(), rows.end(),
                      [](uint32_t x, uint32_t y) { return (x & 0xffffu) < (y & 0xffffu); });
 
-    ripe::VerifyArgs a;
+    // plan every launch first: each one's partial states must fit the workspace
+    const int32_t* lens = cache->lens.data() + (size_t)layer * g.B;
+    const int n_launch = (n_rows + kMaxRowsPerLaunch - 1) / kMaxRowsPerLaunch;
+    std::vector<Plan> plans((size_t)n_launch);
+    for (int l = 0; l < n_launch; ++l) {
+        const int k0 = l * kMaxRowsPerLaunch;
+        const int here = std::min(kMaxRowsPerLaunch, n_rows - k0);
+        plans[l] = make_plan(g, lens, here, rows.data() + k0, draft, cache->tuning);
+        if (plans[l].need > 0) {
+            if (plans[l].need > ws_bytes) return RIPE_EINVAL;
+            if (!d_ws || !aligned(d_ws, 256)) return RIPE_EINVAL;
+        }
+    }
+
+    VerifyArgs a;
     std::memset(&a, 0, sizeof(a));
     const int64_t lk = (int64_t)layer * g.B * g.Hkv;
     a.deep_k = reinterpret_cast<const uint16_t*>(cache->storage + g.off_deep_k) + lk * g.CP * g.d;
@@ -410,23 +333,23 @@ ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
     a.n_sink = n_sink;
     a.w_draft = w_draft;
-    const int32_t* lens = cache->lens.data() + (size_t)layer * g.B;
-    for (int k0 = 0; k0 < n_rows; k0 += ripe::kMaxRowsPerLaunch) {
-        a.rows_here = std::min(ripe::kMaxRowsPerLaunch, n_rows - k0);
+    for (int l = 0; l < n_launch; ++l) {
+        const int k0 = l * kMaxRowsPerLaunch;
+        const Plan& p = plans[l];
+        a.rows_here = std::min(kMaxRowsPerLaunch, n_rows - k0);
         for (int k = 0; k < a.rows_here; ++k) a.rows[k] = rows[k0 + k];
-        const Plan p = make_plan(g, lens, a.rows_here, a.rows, draft);
         a.M = p.M; a.nrb = p.nrb; a.nc = p.nc; a.cl = p.cl; a.cx = p.cx; a.n_groups = p.n_groups;
-        for (int b = 0; b < ripe::kMaxSeqArgs; ++b)
+        for (int b = 0; b < kMaxSeqArgs; ++b)
             a.snc[b] = b < g.B ? (lens[b] > 0 ? (int32_t)((lens[b] + p.cx + p.cl - 1) / p.cl) : 1) : 0;
-        const hipError_t e = p.rows_kernel ? ripe::launch_verify_rows(a, p.rt, p.priv, stream)
-                                           : ripe::launch_verify_keys(a, p.rt, p.wide, stream);
+        const hipError_t e = p.rows_kernel ? launch_verify_rows(a, p.rt, p.priv, stream)
+                                           : launch_verify_keys(a, p.rt, p.wide, stream);
         if (e != hipSuccess) return RIPE_EDEVICE;
-        if (p.nc > 1 && ripe::launch_combine(a, stream) != hipSuccess) return RIPE_EDEVICE;
+        if (p.nc > 1 && launch_combine(a, stream) != hipSuccess) return RIPE_EDEVICE;
     }
     return RIPE_OK;
 }
 
-}  // namespace
+}  // namespace ripe
 
 extern "C" {
 
@@ -435,8 +358,8 @@ ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
                              const void* d_q, ripe_kv_view blk_k, ripe_kv_view blk_v,
                              int32_t n_blk, float* d_out, float* d_lse, void* d_ws,
                              size_t ws_bytes, hipStream_t stream) {
-    return attend(cache, layer, n_rows, h_row_blk, h_row_loop, d_q, blk_k, blk_v, n_blk, 0, -1,
-                  d_out, d_lse, d_ws, ws_bytes, stream);
+    return ripe::attend(cache, layer, n_rows, h_row_blk, h_row_loop, d_q, blk_k, blk_v, n_blk, 0,
+                        -1, d_out, d_lse, d_ws, ws_bytes, false, stream);
 }
 
 ripe_status ripe_draft_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
@@ -445,8 +368,8 @@ ripe_status ripe_draft_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
                             int32_t n_blk, int32_t n_sink, int32_t w_draft, float* d_out,
                             float* d_lse, hipStream_t stream) {
     if (n_sink < 0 || w_draft < 0) return RIPE_EINVAL;
-    return attend(cache, layer, n_rows, h_row_blk, h_row_loop, d_q, blk_k, blk_v, n_blk, n_sink,
-                  w_draft, d_out, d_lse, nullptr, 0, stream);
+    return ripe::attend(cache, layer, n_rows, h_row_blk, h_row_loop, d_q, blk_k, blk_v, n_blk,
+                        n_sink, w_draft, d_out, d_lse, nullptr, 0, false, stream);
 }
 
 const char* ripe_status_string(ripe_status s) {

@@ -1,41 +1,13 @@
 // Internal declarations shared by the host side of the library and its HIP
-// kernels (not part of the public ABI).
+// kernels (not part of the public ABI): kernel arguments and launchers.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "plan.h"
+
 namespace ripe {
-
-constexpr int kTile = 32;          // rows (positions or ring slots) per tile
-constexpr int kMaxBatchPerLaunch = 64;
-constexpr int kMaxRowsPerLaunch = 256;
-constexpr int kMaxSeqArgs = 64;
-
-// Storage geometry derived from a configuration (all counts, no bytes).
-struct Geometry {
-    int32_t n_layers, R, Hq, Hkv, d, W, B, cap, max_block, anchor;
-    int64_t CP;   // deep rows per (layer, seq, head), multiple of 32
-    int64_t WR;   // ring slots in use
-    int64_t WP;   // ring rows allocated, multiple of 32
-    int64_t NR;   // ring planes (R - 1)
-    int64_t off_lens, off_deep_k, off_deep_v, off_ring_k, off_ring_v, total;
-};
-
-// Element offset of (row, dim) inside one tile region, keys and values.
-__host__ __device__ inline int64_t key_off(int64_t row, int e, int d) {
-    return (row >> 5) * (int64_t)(kTile * d) + (e >> 5) * 1024 + (row & 31) * 32 + (e & 31);
-}
-// Column of row k (0..31) of a 32-row value tile.  With this order, the two
-// 16-row halves of a score tile computed by v_mfma_f32_16x16x32_bf16 (lane
-// group q holding rows 4q..4q+3 of each half) feed the value operand of the
-// same instruction as 8 consecutive columns 8q..8q+7.
-__host__ __device__ inline int v_slot(int k) {
-    return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
-}
-__host__ __device__ inline int64_t val_off(int64_t row, int e, int d) {
-    return (row >> 5) * (int64_t)(kTile * d) + (int64_t)e * 32 + v_slot((int)(row & 31));
-}
 
 struct View {            // strided bf16 view, element strides
     const uint16_t* p;
@@ -112,13 +84,10 @@ struct VerifyArgs {
 
 // matrix-core kernels: "keys" (waves split the key tiles of 16*rt row-heads)
 // and "rows" (each wave owns 16*rt row-heads; the workgroup 64*rt)
-int keys_max_row_tiles(int d);
-int rows_max_row_tiles(int d);
 // wide: eight waves instead of four (one workgroup per compute unit; not for
 // the windowed draft)
 hipError_t launch_verify_keys(const VerifyArgs& a, int rt, bool wide, hipStream_t s);
 // priv: four more waves take the ring and draft-block tiles (where rows_private_waves)
-bool rows_private_waves(int d, int rt);
 hipError_t launch_verify_rows(const VerifyArgs& a, int rt, bool priv, hipStream_t s);
 hipError_t launch_combine(const VerifyArgs& a, hipStream_t s);
 

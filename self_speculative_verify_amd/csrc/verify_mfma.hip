@@ -38,6 +38,7 @@
 // A single-chunk item writes O and LSE; otherwise each chunk writes its
 // partial state (m, l, O) and k_combine merges them.
 #include "ripe_internal.h"
+#include "tile_layout.h"
 
 namespace ripe {
 namespace {
@@ -262,7 +263,7 @@ __device__ inline void tile_update(RowTile<D>& rt, const Frags<D>& f, bool full,
     accumulate<D>(rt, f, x, c, rt.m == -INFINITY ? 0.f : rt.m);   // finite reference
 }
 
-// ---------------------------------------------------------------- item// ---------------------------------------------------------------- item
+// ---------------------------------------------------------------- item
 
 struct Item {
     int b, g, c, rb, nc_b;
@@ -1645,9 +1646,6 @@ hipError_t launch_items(K kern, const VerifyArgs& a, hipStream_t s, int threads 
 
 }  // namespace
 
-int keys_max_row_tiles(int d) { return d == 128 ? 1 : 2; }
-int rows_max_row_tiles(int d) { return d == 96 ? 1 : 2; }
-
 hipError_t launch_verify_keys(const VerifyArgs& a, int rt, bool wide, hipStream_t s) {
     if (rt < 1 || rt > keys_max_row_tiles(a.d)) return hipErrorInvalidValue;
     const bool win = a.w_draft >= 0;
@@ -1676,8 +1674,6 @@ hipError_t launch_verify_keys(const VerifyArgs& a, int rt, bool wide, hipStream_
     }
     return hipErrorInvalidValue;
 }
-
-bool rows_private_waves(int d, int rtw) { return d * rtw < 256; }
 
 hipError_t launch_verify_rows(const VerifyArgs& a, int rtw, bool priv, hipStream_t s) {
     if (rtw < 1 || rtw > rows_max_row_tiles(a.d)) return hipErrorInvalidValue;

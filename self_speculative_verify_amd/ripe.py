@@ -20,7 +20,7 @@ __all__ = [
     "RipeConfig", "RipeKVView", "RipeError", "library_path", "load",
     "ripe_cache_bytes", "ripe_section_offset", "ripe_max_batch", "ripe_cache_create", "ripe_destroy",
     "ripe_get_lengths", "ripe_append", "ripe_workspace_bytes", "ripe_verify_attn",
-    "ripe_draft_attn",
+    "ripe_draft_attn", "RipeTuning", "ripe_set_tuning",
     "ripe_status_string", "kv_view", "null_view", "config",
 ]
 
@@ -47,6 +47,12 @@ class RipeConfig(ctypes.Structure):
 class RipeKVView(ctypes.Structure):
     _fields_ = [("ptr", ctypes.c_void_p), ("s_b", ctypes.c_int64), ("s_plane", ctypes.c_int64),
                 ("s_head", ctypes.c_int64), ("s_tok", ctypes.c_int64)]
+
+
+class RipeTuning(ctypes.Structure):
+    """Fixed launch choices of one handle (0 = the planner's choice)."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "kernel", "keys_waves", "row_tiles", "private_waves", "items_target", "min_chunk")]
 
 
 class RipeError(RuntimeError):
@@ -87,6 +93,8 @@ def load():
         L.ripe_draft_attn.restype = I32
         L.ripe_draft_attn.argtypes = [P, I32, I32, P, P, P, RipeKVView, RipeKVView, I32, I32, I32,
                                       P, P, P]
+        L.ripe_set_tuning.restype = I32
+        L.ripe_set_tuning.argtypes = [P, ctypes.POINTER(RipeTuning)]
         L.ripe_status_string.restype = ctypes.c_char_p
         L.ripe_status_string.argtypes = [I32]
         _LIB = L
@@ -163,6 +171,15 @@ def ripe_cache_create(cfg: RipeConfig, storage: torch.Tensor, stream=None) -> ct
 
 def ripe_destroy(handle) -> None:
     load().ripe_destroy(handle)
+
+
+def ripe_set_tuning(handle, tuning: Optional[dict] = None) -> None:
+    """Fix launch choices of a handle (keys of RipeTuning; None restores the planner)."""
+    if tuning is None:
+        _check(load().ripe_set_tuning(handle, None), "ripe_set_tuning")
+        return
+    t = RipeTuning(**tuning)
+    _check(load().ripe_set_tuning(handle, ctypes.byref(t)), "ripe_set_tuning")
 
 
 def ripe_get_lengths(handle, layer: int, batch: int):

@@ -50,3 +50,29 @@ def split_steps(lens: Sequence[int], n_steps: int, rng: np.random.Generator) -> 
         for s in range(n_steps):
             out[s][b] = edges[s + 1] - edges[s]
     return out
+
+
+# Named launch choices for fixtures that run every kernel variant on the same
+# inputs (fields of the C ABI's ripe_tuning; absent fields are the planner's).
+TUNINGS = {
+    "auto": {"items_target": 1},
+    "planner": None,
+    "keys": {"kernel": 1, "items_target": 1},
+    "keys-4waves": {"kernel": 1, "keys_waves": 4},
+    "keys-8waves": {"kernel": 1, "keys_waves": 8, "items_target": 1},
+    "rows": {"kernel": 2, "items_target": 1},
+    "rows-2tiles": {"kernel": 2, "row_tiles": 2, "items_target": 1},
+    "rows-private": {"kernel": 2, "private_waves": 2, "items_target": 1},
+    "rows-noprivate": {"kernel": 2, "private_waves": 1, "items_target": 1},
+    "keys-chunked": {"kernel": 1, "items_target": 100000, "min_chunk": 32},
+    "keys-8waves-chunked": {"kernel": 1, "keys_waves": 8, "items_target": 100000, "min_chunk": 32},
+    "rows-chunked": {"kernel": 2, "items_target": 100000, "min_chunk": 32},
+    "rows-planner": {"kernel": 2},
+    "keys-8waves-planner": {"kernel": 1, "keys_waves": 8},
+}
+
+
+def use_tuning(monkeypatch, name: str) -> None:
+    """Make every RipeCache created from now on use the named launch choices."""
+    from self_speculative_verify_amd import cache as cache_mod
+    monkeypatch.setattr(cache_mod, "DEFAULT_TUNING", TUNINGS[name])

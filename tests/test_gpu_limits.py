@@ -11,6 +11,8 @@ import torch
 import oracle
 from synth import WINDOW_FULL, Workload, grid_rows, ragged_lengths
 
+from helpers import use_tuning
+
 pytestmark = pytest.mark.gpu
 
 TOL_O = 2e-3
@@ -26,19 +28,10 @@ def _gpu():
     yield
 
 
-@pytest.fixture(params=["auto", "keys", "keys-8waves", "rows", "keys-chunked"], autouse=True)
+@pytest.fixture(params=["planner", "keys-4waves", "keys-8waves-planner", "rows-planner", "keys-chunked"],
+                autouse=True)
 def kernel_choice(request, monkeypatch):
-    if request.param in ("keys", "keys-8waves", "keys-chunked"):
-        monkeypatch.setenv("RIPE_KERNEL", "1")
-    if request.param == "keys":
-        monkeypatch.setenv("RIPE_KEYS_WAVES", "4")
-    if request.param == "keys-8waves":
-        monkeypatch.setenv("RIPE_KEYS_WAVES", "8")
-    if request.param == "rows":
-        monkeypatch.setenv("RIPE_KERNEL", "2")
-    if request.param == "keys-chunked":
-        monkeypatch.setenv("RIPE_ITEMS_TARGET", "100000")
-        monkeypatch.setenv("RIPE_MIN_CHUNK", "32")
+    use_tuning(monkeypatch, request.param)
     yield request.param
 
 

@@ -16,7 +16,7 @@ import torch
 import oracle
 from synth import WINDOW_FULL, Workload, f32_to_bf16, grid_rows, named_workload, wave_rows
 
-from helpers import step_arrays
+from helpers import step_arrays, use_tuning
 
 pytestmark = pytest.mark.gpu
 
@@ -34,32 +34,16 @@ def _gpu():
 
 
 # Every case runs through both matrix-core kernels: the planner's choice, and
-# the other one forced (RIPE_KERNEL=1: waves split keys; 2: waves own rows),
-# each with one chunk and with several chunks per sequence (combine kernel),
-# the keys kernel with four and with eight waves, the rows kernel with two row
+# the other one forced (keys: waves split keys; rows: waves own rows), each
+# with one chunk and with several chunks per sequence (combine kernel), the
+# keys kernel with four and with eight waves, the rows kernel with two row
 # tiles per wave where the head size allows, and the rows kernel with and
 # without its private waves (where the head size allows them).
 @pytest.fixture(params=["auto", "keys", "keys-8waves", "rows", "rows-2tiles", "rows-private",
                         "rows-noprivate", "keys-chunked", "keys-8waves-chunked", "rows-chunked"],
                 autouse=True)
 def kernel_choice(request, monkeypatch):
-    kern = {"auto": None, "keys": "1", "keys-8waves": "1", "rows": "2", "rows-2tiles": "2",
-            "rows-private": "2", "rows-noprivate": "2", "keys-chunked": "1",
-            "keys-8waves-chunked": "1", "rows-chunked": "2"}[request.param]
-    if kern:
-        monkeypatch.setenv("RIPE_KERNEL", kern)
-    if request.param.startswith("keys-8waves"):
-        monkeypatch.setenv("RIPE_KEYS_WAVES", "8")
-    if request.param in ("rows-private", "rows-noprivate"):
-        # the rows kernel with and without the private waves for ring and block tiles
-        monkeypatch.setenv("RIPE_PRIV", "2" if request.param == "rows-private" else "1")
-    if request.param == "rows-2tiles":
-        monkeypatch.setenv("RIPE_ROW_TILES", "2")
-    if request.param.endswith("chunked"):
-        monkeypatch.setenv("RIPE_ITEMS_TARGET", "100000")
-        monkeypatch.setenv("RIPE_MIN_CHUNK", "32")
-    else:
-        monkeypatch.setenv("RIPE_ITEMS_TARGET", "1")
+    use_tuning(monkeypatch, request.param)
     yield request.param
 
 

@@ -15,6 +15,8 @@ import oracle
 from synth import Workload, grid_rows, named_workload
 from self_speculative_verify_amd.schedule import batched_verify, draft_pass, per_loop_verify
 
+from helpers import use_tuning
+
 pytestmark = pytest.mark.gpu
 
 TOL_O = 2e-3
@@ -31,14 +33,9 @@ def _gpu():
     yield
 
 
-@pytest.fixture(params=["auto", "keys-chunked", "rows"], autouse=True)
+@pytest.fixture(params=["planner", "keys-chunked", "rows-planner"], autouse=True)
 def kernel_choice(request, monkeypatch):
-    if request.param == "keys-chunked":
-        monkeypatch.setenv("RIPE_KERNEL", "1")
-        monkeypatch.setenv("RIPE_ITEMS_TARGET", "100000")
-        monkeypatch.setenv("RIPE_MIN_CHUNK", "32")
-    elif request.param == "rows":
-        monkeypatch.setenv("RIPE_KERNEL", "2")
+    use_tuning(monkeypatch, request.param)
     yield request.param
 
 
