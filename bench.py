@@ -3,15 +3,22 @@
 
 One step = one verification round: ripe_verify_attn for every recurrent
 layer of the workload (the D x R grid, or the WaveFront diagonal), with the
-committed prefix already resident in HBM.  Steps rotate over several copies
-of the cache so that consecutive reads of one copy are separated by more
-than the 256 MB Infinity Cache.  Each copy's round is captured once in a HIP
-graph; the timed loop replays the graphs between two events.
+committed prefix already resident in HBM.  The default workload is the
+long-context ragged batch (L = 1K-32K, 8 sequences, 32/8 heads, d = 128,
+W = 64, D = 8, R = 32, 4 layers).  Steps rotate over several copies of the
+cache so that consecutive reads of one copy are separated by more than the
+256 MB Infinity Cache.  Each copy's round is captured once in a HIP graph;
+the timed loop replays the graphs between two events.  Caches hold N(0, 1)
+bf16 values drawn on the device (the parity tests use the seeded recipe).
 
 Prints one JSON line: unique-KV GB/s (value), verified tokens/s, the roofline
 of the verify launch (HBM bytes or matrix-core flops, whichever bounds the
-workload), and the fp64 oracle timed on the host cores on a bounded sample
-(whole layers) of the same workload.
+workload), the comparison rounds the workloads are quoted with (the
+Huginn-scale shape at W = 0, 8, 64, 1024; the GQA shape with the deepest
+plane alone and with the full per-loop cache; the small shape in both
+layouts), and the fp64 oracle timed on the host cores on a bounded sample
+(whole layers) of the same workload, plus one layer of the Huginn-scale
+workload on a single thread.
 
 ``--mode per-loop`` times the same step as a forward pass runs it, R calls of
 the D rows of one loop per layer; ``--mode draft`` times the draft pass,
@@ -46,13 +53,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="huginn",
+    ap.add_argument("--workload", default="ragged",
                     choices=["tiny", "huginn", "gqa", "ragged", "wave"])
     ap.add_argument("--window", type=int, default=None, help="W (default: the workload's)")
     ap.add_argument("--full", action="store_true", help="full per-loop cache (W = all)")
     ap.add_argument("--anchor", type=int, default=None)
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the comparison rounds (Huginn-scale windows, GQA deepest-only "
+                         "and full cache, the small shape in both layouts)")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graphs")
     ap.add_argument("--mode", default="batched", choices=["batched", "per-loop", "draft", "wavefront"],
                     help="call schedule: the D x R grid in one call per layer (batched), "
@@ -165,10 +175,11 @@ def time_append(wl, window, anchor, dev, n_rep):
     import ripe_harness as H
     w = wl.replace(n_layers=1, capacity=max(wl.lens) + wl.n_blk * (n_rep + 1))
     cache = H.make_cache(w, device=dev, window=window, anchor=anchor)
-    H.load_prefix(cache, w, device=dev)
-    bk, bv = w.block(0)
-    tbk, tbv = H.to_dev(bk, dev), H.to_dev(bv, dev)
+    fill_random(cache, w, window, dev, seed=4321)
     D, R, B = w.n_blk, w.n_loops, w.batch
+    blk = (B, R, w.n_heads_kv, D, w.head_dim)
+    tbk = torch.randn(blk, device=dev).to(torch.bfloat16)
+    tbv = torch.randn(blk, device=dev).to(torch.bfloat16)
     args = (tbk[:, R - 1, :, :D], tbv[:, R - 1, :, :D],
             tbk[:, :R - 1, :, :D] if R > 1 else None, tbv[:, :R - 1, :, :D] if R > 1 else None)
     torch.cuda.synchronize()
@@ -187,9 +198,10 @@ def time_append(wl, window, anchor, dev, n_rep):
             "GB/s": round(2 * moved / (us * 1e-6) / 1e9, 2), "tokens_per_seq": D}
 
 
-def cpu_baseline(wl, window, anchor, calls, sw=None):
+def cpu_baseline(wl, window, anchor, calls, sw=None, max_layers=None):
     """The fp64 oracle on whole layers of the workload (the same calls, every
-    head), layer after layer until CPU_SAMPLE_S seconds are spent."""
+    head, the seeded inputs of ``synth``), layer after layer until
+    CPU_SAMPLE_S seconds are spent (or max_layers layers)."""
     import numpy as np
     import oracle
     spent, u, n_layers = 0.0, 0, 0
@@ -209,7 +221,7 @@ def cpu_baseline(wl, window, anchor, calls, sw=None):
             u += unique_kv_bytes(wl, window, anchor, c.rows, wl.lens, sw)
         n_layers += 1
         del oc
-        if spent >= CPU_SAMPLE_S:
+        if spent >= CPU_SAMPLE_S or (max_layers and n_layers >= max_layers):
             break
     rounds = n_layers / wl.n_layers
     return {"value": round(u / spent / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
@@ -426,78 +438,64 @@ def wavefront_bench(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the verification path is data-parallel over sequences and KV heads and "
-              "needs no collective; run one process per GPU).", file=sys.stderr)
-        sys.exit(2)
-    if args.capacity_gib > 0:
-        capacity_bench(args)
-        return
-    if args.mode == "wavefront":
-        wavefront_bench(args)
-        return
+def fill_random(cache, wl, window, dev, seed):
+    """Append every sequence's committed prefix to every layer of `cache` with
+    N(0, 1) bf16 keys and values drawn on the device (timing does not depend
+    on the values; the parity tests use the seeded recipe of ``synth``)."""
+    import torch
+    R, H, d, B = wl.n_loops, wl.n_heads_kv, wl.head_dim, wl.batch
+    wr = 0 if R == 1 else min(window, cache.cfg.capacity)
+    T = max(wl.lens)
+    U = min(T, wr)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    for layer in range(wl.n_layers):
+        dk = torch.randn((B, H, T, d), generator=gen, device=dev).to(torch.bfloat16)
+        dv = torch.randn((B, H, T, d), generator=gen, device=dev).to(torch.bfloat16)
+        wk = wv = None
+        if U > 0:
+            wk = torch.randn((B, R - 1, H, U, d), generator=gen, device=dev).to(torch.bfloat16)
+            wv = torch.randn((B, R - 1, H, U, d), generator=gen, device=dev).to(torch.bfloat16)
+        cache.append(layer, wl.lens, dk, dv, wk, wv)
+        del dk, dv, wk, wv
+
+
+def build_setups(wl, window, anchor, calls, copies, dev):
+    """`copies` caches of the workload (each with every layer), with the
+    queries, draft-block planes and outputs of every call."""
     import torch
     import ripe_harness as H
-    from synth import WINDOW_FULL, named_workload
-
-    from self_speculative_verify_amd import schedule
-
-    wl = named_workload(args.workload)
-    window = WINDOW_FULL if args.full else (wl.window if args.window is None else args.window)
-    anchor = wl.anchor if args.anchor is None else args.anchor
     rows = wl.rows
-    if args.mode == "batched":
-        calls = [schedule.Call(list(rows), wl.n_blk)]
-    elif rows != schedule.batched_verify(wl.n_blk, wl.n_loops)[0].rows:
-        print(f"--mode {args.mode} needs a workload that verifies the whole D x R grid",
-              file=sys.stderr)
-        sys.exit(2)
-    elif args.mode == "per-loop":
-        calls = schedule.per_loop_verify(wl.n_blk, wl.n_loops)
-    else:
-        calls = schedule.draft_pass(wl.n_blk, min(args.draft_loops, wl.n_loops))
     call_idx = [[rows.index(x) for x in c.rows] for c in calls]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    # algorithmic bytes and flops of one layer (all its calls)
-    sw = (args.sinks, args.draft_window) if args.mode == "draft" and args.draft_window >= 0 else None
-    u_calls = [unique_kv_bytes(wl, window, anchor, c.rows, wl.lens, sw) for c in calls]
-    f_calls = [flops(wl, c.rows, wl.lens) for c in calls]
-    u_layer, f_layer = sum(u_calls), sum(f_calls)
-    u_round = u_layer * wl.n_layers
-    copies = args.copies or max(2, 1 + math.ceil(2 * MALL_BYTES / max(u_round, 1)))
-    print(f"bench: {wl.name} W={window} anchor={anchor} copies={copies}", file=sys.stderr, flush=True)
-
-    # build the caches (same contents in every copy; host data generated once)
-    memo = {}
-    orig_prefix = wl.prefix
-
-    def prefix(layer, b, n_win=None):
-        key = (layer, b, n_win)
-        if key not in memo:
-            memo[key] = orig_prefix(layer, b, n_win=n_win)
-        return memo[key]
-    wl.prefix = prefix
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
     setups = []
     for c in range(copies):
         cache = H.make_cache(wl, device=dev, window=window, anchor=anchor)
-        H.load_prefix(cache, wl, device=dev)
+        fill_random(cache, wl, window, dev, seed=1000 + c)
         ins = []
         for layer in range(wl.n_layers):
-            q, bk, bv = H.verify_inputs(wl, layer, device=dev)
+            q = torch.randn((wl.batch, len(rows), wl.n_heads_q, wl.head_dim), generator=gen,
+                            device=dev).to(torch.bfloat16)
+            blk = (wl.batch, wl.n_loops, wl.n_heads_kv, wl.max_block, wl.head_dim)
+            bk = torch.randn(blk, generator=gen, device=dev).to(torch.bfloat16)
+            bv = torch.randn(blk, generator=gen, device=dev).to(torch.bfloat16)
             qs = [q if len(calls) == 1 else q[:, idx].contiguous() for idx in call_idx]
             ins.append((qs, bk, bv))
         outs = [[(torch.empty((wl.batch, len(c.rows), wl.n_heads_q, wl.head_dim), device=dev),
                   torch.empty((wl.batch, len(c.rows), wl.n_heads_q), device=dev)) for c in calls]
                 for _ in range(wl.n_layers)]
         setups.append((cache, ins, outs))
-    memo.clear()
-    wl.prefix = orig_prefix
     torch.cuda.synchronize()
+    return setups
+
+
+def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=None):
+    """Step time (ms; each copy's round replayed from a HIP graph, rotating
+    over the copies) and the durations of single calls (ms), timed with
+    events queued behind a spinning kernel so no host gap falls between them."""
+    import torch
+    copies = len(setups)
 
     def run_call(setup, k, layer):
         cache, ins, outs = setup
@@ -521,7 +519,7 @@ def main():
         run_round(s)
     torch.cuda.synchronize()
     graphs = []
-    if not args.eager:
+    if not eager:
         for s in setups:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -530,26 +528,25 @@ def main():
         torch.cuda.synchronize()
 
     def step(k):
-        if args.eager:
+        if eager:
             run_round(setups[k % copies])
         else:
             graphs[k % copies].replay()
 
-    for k in range(args.warmup):
+    for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for k in range(args.steps):
+    for k in range(steps):
         step(k)
     stop.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / max(args.steps, 1)
-    t = ms / 1e3
+    ms = start.elapsed_time(stop) / max(steps, 1)
+    del graphs
 
-    # per-call duration of ripe_verify_attn: events between calls queued
-    # behind a spinning kernel, so no host gap falls between them
-    n_rep = max(1, min(args.steps, 20 if len(calls) == 1 else 2))
+    if n_rep is None:
+        n_rep = max(1, min(steps, 20 if len(calls) == 1 else 2))
     launch_ms = []
     n_ev = len(calls) * wl.n_layers
     for k in range(n_rep):
@@ -562,10 +559,153 @@ def main():
             evs[j + 1].record()
         torch.cuda.synchronize()
         launch_ms += [evs[j].elapsed_time(evs[j + 1]) for j in range(n_ev)]
+    return ms, launch_ms
+
+
+def roofline_of(u_call, f_call, launch_s):
+    """The binding roof of one call (HBM bytes or bf16 matrix flops) and the
+    fraction of it the measured call duration reaches."""
+    if u_call / (HBM_PEAK_GBS * 1e9) >= f_call / (MFMA_BF16_PEAK_TFS * 1e12):
+        roof = {"bound": "hbm", "achieved": round(u_call / launch_s / 1e9, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(f_call / launch_s / 1e12, 2),
+                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    return roof
+
+
+def copies_for(u_round):
+    """Cache copies to rotate so that > 2x the Infinity Cache is read between
+    two reads of one copy (at most 64: rounds that small are bound by launch
+    latency, not by where their bytes come from)."""
+    return min(64, max(2, 1 + math.ceil(2 * MALL_BYTES / max(u_round, 1))))
+
+
+# The comparisons the metric's workloads are quoted with: the Huginn-scale
+# shape at four windows, the GQA shape with the deepest plane alone and with
+# the full per-loop cache, and the small shape in both layouts.
+COMPARISONS = [("huginn", 0), ("huginn", 8), ("huginn", 64), ("huginn", 1024),
+               ("gqa", 0), ("gqa", "full"), ("tiny", 16), ("tiny", "full")]
+
+
+def comparisons(dev, steps, warmup):
+    """One batched verify round of each comparison workload: per-call time,
+    unique-KV GB/s, fraction of HBM and of the binding roof, tokens/s."""
+    import torch
+    from synth import WINDOW_FULL, named_workload
+    from self_speculative_verify_amd import schedule
+    out = {}
+    for name, w in COMPARISONS:
+        wl = named_workload(name)
+        window = WINDOW_FULL if w == "full" else w
+        calls = [schedule.Call(list(wl.rows), wl.n_blk)]
+        u_call = unique_kv_bytes(wl, window, wl.anchor, wl.rows, wl.lens)
+        f_call = flops(wl, wl.rows, wl.lens)
+        copies = copies_for(u_call * wl.n_layers)
+        print(f"bench: comparison {name} W={w} copies={copies}", file=sys.stderr, flush=True)
+        setups = build_setups(wl, window, wl.anchor, calls, copies, dev)
+        ms, launch_ms = time_setups(setups, wl, calls, steps, warmup, n_rep=max(4, min(steps, 10)))
+        del setups
+        torch.cuda.empty_cache()
+        launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+        roof = roofline_of(u_call, f_call, launch_s)
+        out[f"{name}:W={w}"] = {
+            "window": w, "us_per_call": round(launch_s * 1e6, 2), "ms_per_round": round(ms, 5),
+            "unique_kv_bytes_per_call": u_call, "GB/s": round(u_call / launch_s / 1e9, 1),
+            "hbm_frac": round(u_call / launch_s / 1e9 / HBM_PEAK_GBS, 4),
+            "bound": roof["bound"], "frac_of_bound": roof["frac"],
+            "tokens_per_s": round(wl.batch * wl.n_blk / (ms / 1e3), 1)}
+    return out
+
+
+def host_cpu():
+    """CPU model and logical CPU count of the host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def single_thread_baseline():
+    """The oracle on one thread: one layer of the Huginn-scale workload (the
+    D x R grid, every head)."""
+    import oracle
+    from synth import named_workload
+    from self_speculative_verify_amd import schedule
+    wl = named_workload("huginn")
+    n0 = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        r = cpu_baseline(wl, wl.window, wl.anchor, [schedule.Call(list(wl.rows), wl.n_blk)],
+                         max_layers=1)
+    finally:
+        oracle.set_threads(n0)
+    r["workload"] = "huginn"
+    return r
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the verification path is data-parallel over sequences and KV heads and "
+              "needs no collective; run one process per GPU).", file=sys.stderr)
+        sys.exit(2)
+    if args.capacity_gib > 0:
+        capacity_bench(args)
+        return
+    if args.mode == "wavefront":
+        wavefront_bench(args)
+        return
+    import torch
+    from synth import WINDOW_FULL, named_workload
+
+    from self_speculative_verify_amd import schedule
+
+    wl = named_workload(args.workload)
+    window = WINDOW_FULL if args.full else (wl.window if args.window is None else args.window)
+    anchor = wl.anchor if args.anchor is None else args.anchor
+    rows = wl.rows
+    if args.mode == "batched":
+        calls = [schedule.Call(list(rows), wl.n_blk)]
+    elif rows != schedule.batched_verify(wl.n_blk, wl.n_loops)[0].rows:
+        print(f"--mode {args.mode} needs a workload that verifies the whole D x R grid",
+              file=sys.stderr)
+        sys.exit(2)
+    elif args.mode == "per-loop":
+        calls = schedule.per_loop_verify(wl.n_blk, wl.n_loops)
+    else:
+        calls = schedule.draft_pass(wl.n_blk, min(args.draft_loops, wl.n_loops))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # algorithmic bytes and flops of one layer (all its calls)
+    sw = (args.sinks, args.draft_window) if args.mode == "draft" and args.draft_window >= 0 else None
+    u_calls = [unique_kv_bytes(wl, window, anchor, c.rows, wl.lens, sw) for c in calls]
+    f_calls = [flops(wl, c.rows, wl.lens) for c in calls]
+    u_layer, f_layer = sum(u_calls), sum(f_calls)
+    u_round = u_layer * wl.n_layers
+    copies = args.copies or copies_for(u_round)
+    print(f"bench: {wl.name} W={window} anchor={anchor} copies={copies}", file=sys.stderr, flush=True)
+
+    setups = build_setups(wl, window, anchor, calls, copies, dev)
+    print("bench: caches built", file=sys.stderr, flush=True)
+    ms, launch_ms = time_setups(setups, wl, calls, args.steps, args.warmup, args.eager, sw)
+    t = ms / 1e3
     launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     u_call, f_call = u_layer / len(calls), f_layer / len(calls)
-    del setups, graphs
+    del setups
+    torch.cuda.empty_cache()
+    n_rep = max(1, min(args.steps, 20 if len(calls) == 1 else 2))
     append = time_append(wl, window, anchor, dev, n_rep)
+    print("bench: timed", file=sys.stderr, flush=True)
 
     if args.copy_calib:
         n = args.copy_calib << 20
@@ -579,27 +719,29 @@ def main():
     # block positions verified (or, for the draft pass, drafted) per step
     n_tokens = wl.batch * len({i for i, _ in rows})
     gbs = u_round / t / 1e9
-    hbm_time = u_call / (HBM_PEAK_GBS * 1e9)
-    mfma_time = f_call / (MFMA_BF16_PEAK_TFS * 1e12)
     digest = src_digest()
     traffic_key = args.workload if args.mode == "batched" else f"{args.workload}:{args.mode}"
     traffic = (stored_traffic(traffic_key, digest)
                if window == wl.window and anchor == wl.anchor else None)
-    if hbm_time >= mfma_time:
-        roof = {"bound": "hbm", "achieved": round(u_call / launch_s / 1e9, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": round(f_call / launch_s / 1e12, 2),
-                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof = roofline_of(u_call, f_call, launch_s)
     roof["traffic"] = traffic
     roof["launch_us"] = round(launch_s * 1e6, 3)
     roof["algorithmic_bytes"] = round(u_call)
     roof["algorithmic_flops"] = round(f_call)
 
+    comp = None
+    if args.mode == "batched" and not args.no_compare and window == wl.window and anchor == wl.anchor:
+        comp = comparisons(dev, max(5, min(args.steps, 20)), max(2, min(args.warmup, 5)))
+
     cpu = None
     if not args.no_cpu:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, window, anchor, calls, sw)
+        model, ncpu = host_cpu()
+        cpu["cpu_model"] = model
+        cpu["host_cpus"] = ncpu
+        if args.mode == "batched":
+            cpu["single_thread"] = single_thread_baseline()
     u_batched = unique_kv_bytes(wl, window, anchor, rows, wl.lens)
 
     res = {
@@ -616,7 +758,8 @@ def main():
                    **({"draft_window": sw[1], "sinks": sw[0]} if sw is not None else {}),
                    "rows_per_call": len(rows) // len(calls),
                    "anchor": "query" if anchor == 0 else "cache",
-                   "cache_copies": copies, "timing": "eager" if args.eager else "hip-graph"},
+                   "cache_copies": copies, "timing": "eager" if args.eager else "hip-graph",
+                   "values": "N(0,1) bf16 drawn on the device"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(n_tokens / t, 1),
         "bytes_vs_batched": round(u_layer / u_batched, 4),
@@ -625,6 +768,7 @@ def main():
         "kernel_sources": digest,
         "roofline": roof,
         "append": append,
+        "comparisons": comp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -13,10 +13,13 @@ statistic; shapes come from the named workloads):
 * plane r < R: ``K_r = K_R + rho**(R - r) * N(0, 1)`` (same for V), so the
   planes approach the last one geometrically as r grows (RIPE abstract, second
   sentence: 0.88 and 0.81 per loop);
-* heavy tails: ``round(0.01 * L)`` positions per (layer, sequence), drawn
-  without replacement from [0, L), get their r < R offsets scaled by 30 (RIPE
-  abstract, third sentence: 1% of positions carry most of the deepest-plane
-  error);
+* heavy tails: 1% of the tail positions, ``round(0.01 * (L - W))`` per
+  (layer, sequence) with W the workload's own window, drawn without
+  replacement from the tail [0, L - W), get their r < R offsets scaled by 30
+  (RIPE abstract, third sentence: 1% of positions carry most of the
+  deepest-plane error).  A RIPE cache with that window stores only the
+  deepest plane of those positions; the full per-loop cache (or a wider
+  window) reads their scaled planes;
 * queries: N(0, 1).
 
 The module holds no cache-layout or attention arithmetic.
@@ -144,12 +147,14 @@ class Workload:
         return x.reshape(POS_BLOCK, nr, self.n_heads_kv, self.head_dim)
 
     def heavy_positions(self, layer: int, b: int) -> np.ndarray:
-        L = self.lens[b]
-        n = int(round(self.heavy_frac * L))
-        if n == 0 or L == 0:
+        """Heavy-tail positions of a sequence: drawn from its tail [0, L - W)
+        (W: the workload's window)."""
+        tail = max(self.lens[b] - min(self.window, self.lens[b]), 0)
+        n = int(round(self.heavy_frac * tail))
+        if n == 0:
             return np.zeros(0, dtype=np.int64)
         rng = np.random.default_rng(np.random.SeedSequence([self.seed, layer, b, _HEAVY]))
-        return np.sort(rng.choice(L, size=n, replace=False)).astype(np.int64)
+        return np.sort(rng.choice(tail, size=n, replace=False)).astype(np.int64)
 
     def planes(self, layer: int, b: int, p0: int, p1: int,
                loops: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:

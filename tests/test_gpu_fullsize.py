@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from synth import named_workload
+from synth import WINDOW_FULL, grid_rows, named_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -43,21 +43,24 @@ def _sample_mask(wl, seed):
     return want
 
 
-@pytest.mark.parametrize("name", ["tiny", "huginn", "gqa", "ragged", "wave"])
-def test_full_size_sampled(name):
+def _run_full(wl, window=None, seed=4242, want=None):
+    """Prefix append and one verify call of layer 0 at full size (planner
+    defaults); layout compared whole, outputs on a seeded sample."""
     import ripe_harness as H
-    wl = named_workload(name).replace(n_layers=1)
-    print(f"full-size {name}: batch {wl.batch}, lens {wl.lens if wl.batch <= 8 else '...'}, "
-          f"rows {wl.n_rows}, heads {wl.n_heads_q}/{wl.n_heads_kv}, d {wl.head_dim}, W {wl.window}",
+    window = wl.window if window is None else window
+    print(f"full-size {wl.name}: batch {wl.batch}, lens {wl.lens if wl.batch <= 8 else '...'}, "
+          f"rows {wl.n_rows}, heads {wl.n_heads_q}/{wl.n_heads_kv}, d {wl.head_dim}, W {window}",
           flush=True)
-    cache = H.make_cache(wl)
+    cache = H.make_cache(wl, window=window)
     H.load_prefix(cache, wl)
     q, bk, bv = H.verify_inputs(wl, 0)
     out, lse = cache.verify(0, wl.rows, q, bk, bv, wl.n_blk)
     torch.cuda.synchronize()
-    oc = oracle.prefix_cache(wl, layers=[0])
+    oc = oracle.prefix_cache(wl, layers=[0], window=window)
     assert np.array_equal(cache.storage.cpu().numpy(), oc.image), "layout differs from the oracle"
-    want = _sample_mask(wl, 4242)
+    del cache
+    if want is None:
+        want = _sample_mask(wl, seed)
     ref_o, ref_l = oc.verify(0, wl.rows, wl.queries(0), *wl.block(0), wl.n_blk, want=want)
     sel = want.astype(bool)
     o = out.cpu().double().numpy()[sel]
@@ -65,10 +68,37 @@ def test_full_size_sampled(name):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
     err_o = float(np.max(np.abs(o - ref_o[sel])))
     err_l = float(np.max(np.abs(l - ref_l[sel]) / np.maximum(1.0, np.abs(ref_l[sel]))))
-    print(f"full-size {name}: {int(sel.sum())} outputs, max|dO|={err_o:.3e} max rel dLSE={err_l:.3e}",
-          flush=True)
+    print(f"full-size {wl.name} W={window}: {int(sel.sum())} outputs, max|dO|={err_o:.3e} "
+          f"max rel dLSE={err_l:.3e}", flush=True)
     assert err_o <= TOL_O
     assert err_l <= TOL_LSE
+
+
+@pytest.mark.parametrize("name", ["tiny", "huginn", "gqa", "ragged", "wave"])
+def test_full_size_sampled(name):
+    _run_full(named_workload(name).replace(n_layers=1))
+
+
+# the windows the Huginn-scale workload is compared at besides its own (64),
+# and the GQA workload's full per-loop cache (every position at all 32 loops)
+@pytest.mark.parametrize("name,window", [("huginn", 0), ("huginn", 8), ("huginn", 1024),
+                                         ("gqa", WINDOW_FULL)])
+@pytest.mark.timeout(600)
+def test_full_size_other_windows(name, window):
+    _run_full(named_workload(name).replace(n_layers=1), window=window, seed=4400 + (window % 4099))
+
+
+def test_full_size_gqa_288_rows():
+    """The GQA shape with a 9-token block: 9 x 32 = 288 rows, so the call runs
+    a launch of 256 rows and one of the 32 left; the short one splits the
+    committed positions into chunks and needs the workspace (its size must
+    cover that launch too).  Sampled outputs include every row of the second
+    launch (loops 29..32) at one head."""
+    wl = named_workload("gqa", n_layers=1, n_blk=9, rows=grid_rows(9, 32))
+    want = _sample_mask(wl, 4545)
+    late = [k for k, (i, r) in enumerate(wl.rows) if r >= 29]
+    want[:, late, 5] = 1
+    _run_full(wl, want=want)
 
 
 def test_full_size_ragged_append_then_verify():
