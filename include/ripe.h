@@ -58,7 +58,9 @@ typedef enum {
     RIPE_OK = 0,
     RIPE_EINVAL = 1,    /* bad configuration, pointer, stride, row or size */
     RIPE_ECAPACITY = 2, /* an append would pass the capacity; nothing written */
-    RIPE_EDEVICE = 3    /* a HIP call or kernel launch failed */
+    RIPE_EDEVICE = 3,   /* a HIP call or kernel launch failed */
+    RIPE_ESCRATCH = 4   /* ripe_verify_attn_noalloc: the call needs more than
+                           the library's fixed scratch (nothing enqueued) */
 } ripe_status;
 
 typedef enum { RIPE_ANCHOR_QUERY = 0, RIPE_ANCHOR_CACHE = 1 } ripe_anchor;
@@ -236,6 +238,29 @@ ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
                              const void* d_q, ripe_kv_view blk_k, ripe_kv_view blk_v,
                              int32_t n_blk, float* d_out, float* d_lse, void* d_ws,
                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ripe_verify_attn without a caller workspace and without any allocation, for
+ * callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The partial softmax states of split
+ * key ranges go to a fixed scratch array inside the library, one per device,
+ * of RIPE_NOALLOC_SCRATCH_BYTES; the device holds it until the process ends.
+ * A call whose launches need more than that returns RIPE_ESCRATCH with
+ * nothing enqueued (ripe_workspace_bytes bounds the need).  Arguments,
+ * results and every other error are those of ripe_verify_attn.  Every call on
+ * one device shares that device's scratch: calls that overlap on one device
+ * (different streams, or different threads without ordering) race and give
+ * wrong results; calls ordered on one stream are safe.  Nothing in the
+ * scratch needs clearing between calls (every partial state a launch reads
+ * was written by the same launch sequence).  The first call on a device looks
+ * up that device's scratch address (hipGetSymbolAddress) and keeps it.
+ */
+#define RIPE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ripe_status ripe_verify_attn_noalloc(ripe_cache* cache, int32_t layer, int32_t n_rows,
+                                     const int32_t* h_row_blk, const int32_t* h_row_loop,
+                                     const void* d_q, ripe_kv_view blk_k, ripe_kv_view blk_v,
+                                     int32_t n_blk, float* d_out, float* d_lse,
+                                     hipStream_t stream);
 
 /*
  * Windowed draft attention of one layer (page "Windowed-MTP: Removing the

@@ -12,6 +12,7 @@ namespace ripe {
 constexpr int kTile = 32;          // rows (positions or ring slots) per tile
 constexpr int kMaxBatchPerLaunch = 64;
 constexpr int kMaxRowsPerLaunch = 256;
+constexpr int kMaxRowsPerCall = 65535;
 constexpr int kMaxSeqArgs = 64;
 
 // Storage geometry derived from a configuration (all counts, no bytes).

@@ -23,6 +23,11 @@ struct ripe_cache {
     uint8_t* storage;
     std::vector<int32_t> lens;   // [n_layers][B], host copy of the lens section
     ripe::Tuning tuning;         // all zero: the planner decides
+    int device;                  // device of the storage (-1 until first needed)
+    // sorted row words and launch plans of a call, sized once at creation
+    // for the largest call, so that a verification call allocates nothing
+    std::vector<uint32_t> rows_buf;
+    std::vector<ripe::Plan> plans_buf;
 };
 
 namespace {
@@ -150,6 +155,9 @@ ripe_status ripe_cache_create(const ripe_config* cfg, void* d_storage, size_t by
     c->storage = static_cast<uint8_t*>(d_storage);
     c->lens.assign((size_t)g.n_layers * g.B, 0);
     std::memset(&c->tuning, 0, sizeof(c->tuning));
+    c->device = -1;
+    c->rows_buf.assign(ripe::kMaxRowsPerCall, 0u);
+    c->plans_buf.resize((ripe::kMaxRowsPerCall + ripe::kMaxRowsPerLaunch - 1) / ripe::kMaxRowsPerLaunch);
     if (hipMemsetAsync(d_storage, 0, (size_t)g.total, stream) != hipSuccess) {
         delete c;
         return RIPE_EDEVICE;
@@ -255,7 +263,7 @@ ripe_status ripe_append(ripe_cache* cache, int32_t layer, const int32_t* h_n_new
 }
 
 size_t ripe_workspace_bytes(const ripe_cache* cache, int32_t n_rows) {
-    if (!live(cache) || n_rows <= 0 || n_rows > 65535) return 0;
+    if (!live(cache) || n_rows <= 0 || n_rows > ripe::kMaxRowsPerCall) return 0;
     return ripe::workspace_bound(cache->g, cache->lens.data(), n_rows, cache->tuning);
 }
 
@@ -263,11 +271,13 @@ size_t ripe_workspace_bytes(const ripe_cache* cache, int32_t n_rows) {
 
 namespace ripe {
 
-// ripe_verify_attn (n_sink = 0, w_draft = -1) and ripe_draft_attn.  ws_fixed:
-// d_ws is a buffer of ws_bytes bytes that is refused only when one of the
-// call's launches needs more than that; otherwise the caller's workspace must
-// hold at least ripe_workspace_bytes for this row count.  Every argument and
-// every launch's partial-state size is checked before the first launch.
+// ripe_verify_attn (n_sink = 0, w_draft = -1), ripe_draft_attn and
+// ripe_verify_attn_noalloc.  ws_fixed: d_ws is the library's fixed scratch of
+// ws_bytes bytes, and a call is refused (RIPE_ESCRATCH) only when one of its
+// launches needs more than that; otherwise the caller's workspace must hold
+// at least ripe_workspace_bytes for this row count.  Every argument and every
+// launch's partial-state size is checked before the first launch.  Uses the
+// handle's preallocated row and plan buffers: no allocation of any kind.
 ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32_t* h_row_blk,
                    const int32_t* h_row_loop, const void* d_q, ripe_kv_view blk_k,
                    ripe_kv_view blk_v, int32_t n_blk, int32_t n_sink, int32_t w_draft,
@@ -276,7 +286,7 @@ ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32
     const bool draft = w_draft >= 0;
     if (!live(cache) || layer < 0 || layer >= cache->g.n_layers) return RIPE_EINVAL;
     const Geometry& g = cache->g;
-    if (n_rows < 0 || n_rows > 65535) return RIPE_EINVAL;
+    if (n_rows < 0 || n_rows > kMaxRowsPerCall) return RIPE_EINVAL;
     if (n_rows == 0) return RIPE_OK;
     if (!h_row_blk || !h_row_loop || !d_q || !d_out || !d_lse) return RIPE_EINVAL;
     if (n_blk < 1 || n_blk > g.max_block) return RIPE_EINVAL;
@@ -293,22 +303,25 @@ ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32
 
     // rows sorted by (loop, block offset) so that rows reading the same planes
     // are adjacent
-    std::vector<uint32_t> rows((size_t)n_rows);
+    uint32_t* rows = cache->rows_buf.data();
     for (int k = 0; k < n_rows; ++k)
         rows[k] = (uint32_t)h_row_blk[k] | ((uint32_t)h_row_loop[k] << 8) | ((uint32_t)k << 16);
-    std::stable_sort(rows.begin(), rows.end(),
-                     [](uint32_t x, uint32_t y) { return (x & 0xffffu) < (y & 0xffffu); });
+    // (loop and offset first, then the row index in bits 16..31: the order a
+    // stable sort would give, without its temporary buffer)
+    std::sort(rows, rows + n_rows, [](uint32_t x, uint32_t y) {
+        return ((x << 16) | (x >> 16)) < ((y << 16) | (y >> 16));
+    });
 
     // plan every launch first: each one's partial states must fit the workspace
     const int32_t* lens = cache->lens.data() + (size_t)layer * g.B;
     const int n_launch = (n_rows + kMaxRowsPerLaunch - 1) / kMaxRowsPerLaunch;
-    std::vector<Plan> plans((size_t)n_launch);
+    Plan* plans = cache->plans_buf.data();
     for (int l = 0; l < n_launch; ++l) {
         const int k0 = l * kMaxRowsPerLaunch;
         const int here = std::min(kMaxRowsPerLaunch, n_rows - k0);
-        plans[l] = make_plan(g, lens, here, rows.data() + k0, draft, cache->tuning);
+        plans[l] = make_plan(g, lens, here, rows + k0, draft, cache->tuning);
         if (plans[l].need > 0) {
-            if (plans[l].need > ws_bytes) return RIPE_EINVAL;
+            if (plans[l].need > ws_bytes) return ws_fixed ? RIPE_ESCRATCH : RIPE_EINVAL;
             if (!d_ws || !aligned(d_ws, 256)) return RIPE_EINVAL;
         }
     }
@@ -349,6 +362,18 @@ ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32
     return RIPE_OK;
 }
 
+ripe_status cache_device(ripe_cache* cache, int* device) {
+    if (!live(cache)) return RIPE_EINVAL;
+    if (cache->device < 0) {
+        hipPointerAttribute_t attr;
+        if (hipPointerGetAttributes(&attr, cache->storage) != hipSuccess) return RIPE_EDEVICE;
+        if (attr.device < 0) return RIPE_EDEVICE;
+        cache->device = attr.device;
+    }
+    *device = cache->device;
+    return RIPE_OK;
+}
+
 }  // namespace ripe
 
 extern "C" {
@@ -378,6 +403,7 @@ const char* ripe_status_string(ripe_status s) {
         case RIPE_EINVAL: return "invalid argument";
         case RIPE_ECAPACITY: return "append exceeds capacity";
         case RIPE_EDEVICE: return "HIP launch or runtime error";
+        case RIPE_ESCRATCH: return "call needs more scratch than the library's fixed buffer";
     }
     return "unknown status";
 }

@@ -92,3 +92,22 @@ hipError_t launch_verify_rows(const VerifyArgs& a, int rt, bool priv, hipStream_
 hipError_t launch_combine(const VerifyArgs& a, hipStream_t s);
 
 }  // namespace ripe
+
+// ---------------------------------------------------------------- host side
+
+#include "ripe.h"
+
+namespace ripe {
+
+// Verification attention of one call after full validation (see ripe_api.cpp);
+// ws_fixed: d_ws is the library's fixed scratch, refused with RIPE_ESCRATCH
+// when a launch needs more than ws_bytes.
+ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32_t* h_row_blk,
+                   const int32_t* h_row_loop, const void* d_q, ripe_kv_view blk_k,
+                   ripe_kv_view blk_v, int32_t n_blk, int32_t n_sink, int32_t w_draft,
+                   float* d_out, float* d_lse, void* d_ws, size_t ws_bytes, bool ws_fixed,
+                   hipStream_t stream);
+// Device of a live handle's storage (looked up once).
+ripe_status cache_device(ripe_cache* cache, int* device);
+
+}  // namespace ripe

@@ -13,7 +13,8 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "RIPE_OK", "RIPE_EINVAL", "RIPE_ECAPACITY", "RIPE_EDEVICE",
+    "RIPE_OK", "RIPE_EINVAL", "RIPE_ECAPACITY", "RIPE_EDEVICE", "RIPE_ESCRATCH",
+    "RIPE_NOALLOC_SCRATCH_BYTES", "ripe_verify_attn_noalloc",
     "RIPE_ANCHOR_QUERY", "RIPE_ANCHOR_CACHE", "RIPE_WINDOW_FULL",
     "RIPE_SECTION_LENS", "RIPE_SECTION_DEEP_K", "RIPE_SECTION_DEEP_V",
     "RIPE_SECTION_RING_K", "RIPE_SECTION_RING_V", "RIPE_SECTION_END",
@@ -24,7 +25,8 @@ __all__ = [
     "ripe_status_string", "kv_view", "null_view", "config",
 ]
 
-RIPE_OK, RIPE_EINVAL, RIPE_ECAPACITY, RIPE_EDEVICE = 0, 1, 2, 3
+RIPE_OK, RIPE_EINVAL, RIPE_ECAPACITY, RIPE_EDEVICE, RIPE_ESCRATCH = 0, 1, 2, 3, 4
+RIPE_NOALLOC_SCRATCH_BYTES = 64 << 20
 RIPE_ANCHOR_QUERY, RIPE_ANCHOR_CACHE = 0, 1
 RIPE_WINDOW_FULL = 2**31 - 1
 (RIPE_SECTION_LENS, RIPE_SECTION_DEEP_K, RIPE_SECTION_DEEP_V, RIPE_SECTION_RING_K,
@@ -90,6 +92,9 @@ def load():
         L.ripe_verify_attn.restype = I32
         L.ripe_verify_attn.argtypes = [P, I32, I32, P, P, P, RipeKVView, RipeKVView, I32,
                                        P, P, P, SZ, P]
+        L.ripe_verify_attn_noalloc.restype = I32
+        L.ripe_verify_attn_noalloc.argtypes = [P, I32, I32, P, P, P, RipeKVView, RipeKVView, I32,
+                                               P, P, P]
         L.ripe_draft_attn.restype = I32
         L.ripe_draft_attn.argtypes = [P, I32, I32, P, P, P, RipeKVView, RipeKVView, I32, I32, I32,
                                       P, P, P]
@@ -215,6 +220,23 @@ def ripe_verify_attn(handle, layer: int, row_blk: Sequence[int], row_loop: Seque
                                    blk_k, blk_v, n_blk, ctypes.c_void_p(out.data_ptr()),
                                    ctypes.c_void_p(lse.data_ptr()), ws_ptr, ws_bytes,
                                    _stream(stream)), "ripe_verify_attn")
+
+
+def ripe_verify_attn_noalloc(handle, layer: int, row_blk: Sequence[int], row_loop: Sequence[int],
+                             q: torch.Tensor, blk_k: RipeKVView, blk_v: RipeKVView, n_blk: int,
+                             out: torch.Tensor, lse: torch.Tensor, stream=None) -> None:
+    """ripe_verify_attn with the library's fixed scratch instead of a workspace."""
+    if len(row_blk) != len(row_loop):
+        raise ValueError("row_blk and row_loop differ in length")
+    for t, name, dt in ((q, "q", torch.bfloat16), (out, "out", torch.float32),
+                        (lse, "lse", torch.float32)):
+        if not t.is_cuda or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    _check(load().ripe_verify_attn_noalloc(handle, layer, len(row_blk), _i32_array(row_blk),
+                                           _i32_array(row_loop), ctypes.c_void_p(q.data_ptr()),
+                                           blk_k, blk_v, n_blk, ctypes.c_void_p(out.data_ptr()),
+                                           ctypes.c_void_p(lse.data_ptr()), _stream(stream)),
+           "ripe_verify_attn_noalloc")
 
 
 def ripe_draft_attn(handle, layer: int, row_blk: Sequence[int], row_loop: Sequence[int],

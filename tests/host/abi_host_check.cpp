@@ -50,6 +50,12 @@ extern "C" hipError_t hipMemsetAsync(void* p, int v, size_t n, hipStream_t) {
     return hipSuccess;
 }
 
+extern "C" hipError_t hipPointerGetAttributes(hipPointerAttribute_t* a, const void*) {
+    std::memset(a, 0, sizeof(*a));
+    a->device = 0;
+    return hipSuccess;
+}
+
 namespace ripe {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t) {
