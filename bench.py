@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--anchor", type=int, default=None)
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--tuning", default=None, metavar="JSON",
+                    help="fixed launch choices for every cache (fields of ripe_tuning), e.g. "
+                         "'{\"rows_waves\": 4}'")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the comparison rounds (Huginn-scale windows, GQA deepest-only "
                          "and full cache, the small shape in both layouts)")
@@ -685,6 +688,9 @@ def main():
         calls = schedule.draft_pass(wl.n_blk, min(args.draft_loops, wl.n_loops))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.tuning:
+        from self_speculative_verify_amd import cache as cache_mod
+        cache_mod.DEFAULT_TUNING = json.loads(args.tuning)
 
     # algorithmic bytes and flops of one layer (all its calls)
     sw = (args.sinks, args.draft_window) if args.mode == "draft" and args.draft_window >= 0 else None
@@ -759,7 +765,8 @@ def main():
                    "rows_per_call": len(rows) // len(calls),
                    "anchor": "query" if anchor == 0 else "cache",
                    "cache_copies": copies, "timing": "eager" if args.eager else "hip-graph",
-                   "values": "N(0,1) bf16 drawn on the device"},
+                   "values": "N(0,1) bf16 drawn on the device",
+                   **({"tuning": json.loads(args.tuning)} if args.tuning else {})},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(n_tokens / t, 1),
         "bytes_vs_batched": round(u_layer / u_batched, 4),

@@ -40,7 +40,8 @@ int64_t extra_tiles(const Geometry& g, const uint32_t* rows, int rows_here, int 
 
 int keys_max_row_tiles(int d) { return d == 128 ? 1 : 2; }
 int rows_max_row_tiles(int d) { return d == 96 ? 1 : 2; }
-bool rows_private_waves(int d, int rtw) { return d * rtw < 256; }
+// (instantiated at head_dim 64 and 96)
+bool rows_private_waves(int d, int rtw) { return d != 128 && d * rtw < 256; }
 
 // Row-heads (query row x query head of a KV group) of a KV head: with 128 or
 // more the "rows" kernel gives each wave 16*rt of them and a workgroup 64*rt;
