@@ -255,7 +255,7 @@ ripe_status ripe_verify_attn(ripe_cache* cache, int32_t layer, int32_t n_rows,
  * was written by the same launch sequence).  The first call on a device looks
  * up that device's scratch address (hipGetSymbolAddress) and keeps it.
  */
-#define RIPE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define RIPE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 ripe_status ripe_verify_attn_noalloc(ripe_cache* cache, int32_t layer, int32_t n_rows,
                                      const int32_t* h_row_blk, const int32_t* h_row_loop,
                                      const void* d_q, ripe_kv_view blk_k, ripe_kv_view blk_v,

@@ -54,7 +54,9 @@ bool rows_private_waves(int d, int rtw) { return d != 128 && d * rtw < 256; }
 // little next to the keys they read.  Short keys items instead go unsplit to
 // an eight-wave workgroup.  The last chunk of a sequence also takes the ring
 // and draft-block tiles of its row block, so it reads cx fewer committed
-// positions than the others.
+// positions than the others.  When one round of the rows kernel's row blocks
+// already fills the chip, sequences far longer than the mean load of a slot
+// are split as well (see below).
 Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint32_t* rows,
                bool draft, const Tuning& t) {
     Plan p;
@@ -111,6 +113,23 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
         cl = std::max<int64_t>(min_chunk, up((sum + pairs - 1) / std::max<int64_t>(pairs, 1), 32));
         // a bound on the chunk count that never falls as rows or lengths grow
         nc_cap = std::max<int64_t>(1, std::min<int64_t>(pairs, (lmax + cx + min_chunk - 1) / min_chunk));
+    } else if (p.rows_kernel && !draft && !t.items_target) {
+        // One round of row blocks fills the chip, but a sequence much longer
+        // than the mean load of a workgroup slot would still finish last (a
+        // ragged batch): split the sequences into chunks no longer than that
+        // mean, and the launch hands out the longest items first.
+        int64_t sum = 0, sum_l = 0;
+        for (int b = 0; b < g.B; ++b)
+            if (lens[b] > 0) {
+                sum += lens[b] + cx;
+                sum_l += lens[b];
+            }
+        const int64_t mean = (units * sum + slots - 1) / slots;
+        if (lmax + cx > mean + mean / 8) cl = std::max<int64_t>(min_chunk, up(mean, 32));
+        // for any row set of this size (cx at most this one): chunks are never
+        // shorter than the mean without cx
+        const int64_t cl_lb = std::max<int64_t>(min_chunk, up((units * sum_l + slots - 1) / slots, 32));
+        if (lmax + cx > cl_lb + cl_lb / 8) nc_cap = std::max<int64_t>(1, (lmax + cx + cl_lb - 1) / cl_lb);
     }
     if (cl == 0 || cl >= lmax + cx) {
         p.cx = 0;
@@ -124,7 +143,7 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
     p.n_groups = (int)(heads * p.nc);
     const size_t state = (size_t)p.M * (g.d + 2) * sizeof(float);   // one chunk of a KV head
     p.need = p.nc > 1 ? (size_t)heads * p.nc * state : 0;
-    p.bound = base < slots ? (size_t)heads * nc_cap * state : 0;
+    p.bound = nc_cap > 1 ? (size_t)heads * nc_cap * state : 0;
     return p;
 }
 

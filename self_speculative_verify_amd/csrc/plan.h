@@ -14,6 +14,7 @@ constexpr int kMaxBatchPerLaunch = 64;
 constexpr int kMaxRowsPerLaunch = 256;
 constexpr int kMaxRowsPerCall = 65535;
 constexpr int kMaxSeqArgs = 64;
+constexpr int kMaxPairs = 256;     // (sequence, chunk) items listed in a launch's arguments
 
 // Storage geometry derived from a configuration (all counts, no bytes).
 struct Geometry {

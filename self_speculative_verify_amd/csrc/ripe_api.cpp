@@ -271,6 +271,35 @@ size_t ripe_workspace_bytes(const ripe_cache* cache, int32_t n_rows) {
 
 namespace ripe {
 
+// The (sequence, chunk) items of a split launch, longest first (stable), in
+// the launch's arguments: workgroups start in that order, so the longest items
+// do not start last.  Only for at most kMaxSeqArgs sequences and kMaxPairs
+// items; otherwise the launch enumerates (sequence, KV head, chunk) in order.
+void order_pairs(VerifyArgs& a, const int32_t* lens, int B) {
+    a.n_pairs = 0;
+    if (a.nc <= 1 || B > kMaxSeqArgs || a.nc > 1024) return;
+    int n = 0;
+    for (int b = 0; b < B; ++b) n += a.snc[b];
+    if (n > kMaxPairs) return;
+    int64_t len[kMaxPairs];
+    n = 0;
+    for (int b = 0; b < B; ++b)
+        for (int c = 0; c < a.snc[b]; ++c) {
+            // positions of work: a whole chunk, or what the last one holds
+            const int64_t work = lens[b] > 0 ? std::min<int64_t>(a.cl, lens[b] + a.cx - (int64_t)c * a.cl) : 0;
+            int k = n++;
+            while (k > 0 && len[k - 1] < work) {     // insertion: longest first, stable
+                len[k] = len[k - 1];
+                a.pairs[k] = a.pairs[k - 1];
+                --k;
+            }
+            len[k] = work;
+            a.pairs[k] = (uint16_t)(b | (c << 6));
+        }
+    a.n_pairs = n;
+    a.n_groups = n * a.Hkv;
+}
+
 // ripe_verify_attn (n_sink = 0, w_draft = -1), ripe_draft_attn and
 // ripe_verify_attn_noalloc.  ws_fixed: d_ws is the library's fixed scratch of
 // ws_bytes bytes, and a call is refused (RIPE_ESCRATCH) only when one of its
@@ -354,6 +383,7 @@ ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32
         a.M = p.M; a.nrb = p.nrb; a.nc = p.nc; a.cl = p.cl; a.cx = p.cx; a.n_groups = p.n_groups;
         for (int b = 0; b < kMaxSeqArgs; ++b)
             a.snc[b] = b < g.B ? (lens[b] > 0 ? (int32_t)((lens[b] + p.cx + p.cl - 1) / p.cl) : 1) : 0;
+        order_pairs(a, lens, g.B);
         const hipError_t e = p.rows_kernel ? launch_verify_rows(a, p.rt, p.priv, stream)
                                            : launch_verify_keys(a, p.rt, p.wide, stream);
         if (e != hipSuccess) return RIPE_EDEVICE;

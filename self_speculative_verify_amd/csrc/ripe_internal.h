@@ -72,7 +72,7 @@ struct VerifyArgs {
     // windowed draft attention: a row (i, r) keeps the committed keys
     // s < n_sink or s >= L + i - w_draft; w_draft < 0: every committed key
     int32_t n_sink, w_draft;
-    int32_t n_groups;        // B * Hkv * nc
+    int32_t n_groups;        // B * Hkv * nc, or n_pairs * Hkv
     // rows of this launch sorted by (loop, block offset):
     // bits 0..7 block offset, 8..15 loop, 16..31 row index in the call
     uint32_t rows[kMaxRowsPerLaunch];
@@ -80,6 +80,10 @@ struct VerifyArgs {
     // sequences (0: read the length from storage); the host's copy of the
     // lengths advances in stream order with the one in storage
     int32_t snc[kMaxSeqArgs];
+    // when n_pairs > 0: the (sequence, chunk) items of a split launch, longest
+    // first (bits 0..5 sequence, 6..15 chunk), so the longest start first
+    int32_t n_pairs;
+    uint16_t pairs[kMaxPairs];
 };
 
 // matrix-core kernels: "keys" (waves split the key tiles of 16*rt row-heads)

@@ -273,16 +273,25 @@ struct Item {
 };
 
 // XCD-aware decode: the row blocks of one (b, g, chunk) share blockIdx % 8,
-// so they run on one XCD and share its L2.
+// so they run on one XCD and share its L2.  Groups are dispatched in
+// blockIdx order; with a pair list, group k is KV head k % Hkv of the
+// (sequence, chunk) pair k / Hkv of the list, which puts the longest first.
 __device__ inline bool decode_item(const VerifyArgs& a, Item& it) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int grp = (slot / a.nrb) * 8 + xcd;
     it.rb = slot % a.nrb;
     if (grp >= a.n_groups) return false;
-    it.c = grp % a.nc;
-    const int bg = grp / a.nc;
-    it.g = bg % a.Hkv;
-    it.b = bg / a.Hkv;
+    if (a.n_pairs > 0) {
+        const int pr = a.pairs[grp / a.Hkv];
+        it.g = grp % a.Hkv;
+        it.b = pr & 63;
+        it.c = pr >> 6;
+    } else {
+        it.c = grp % a.nc;
+        const int bg = grp / a.nc;
+        it.g = bg % a.Hkv;
+        it.b = bg / a.Hkv;
+    }
     it.L = a.lens[it.b];
     it.nc_b = it.L > 0 ? (int)((it.L + a.cx + a.cl - 1) / a.cl) : 1;
     if (it.c >= it.nc_b) return false;

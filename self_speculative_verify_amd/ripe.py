@@ -26,7 +26,7 @@ __all__ = [
 ]
 
 RIPE_OK, RIPE_EINVAL, RIPE_ECAPACITY, RIPE_EDEVICE, RIPE_ESCRATCH = 0, 1, 2, 3, 4
-RIPE_NOALLOC_SCRATCH_BYTES = 64 << 20
+RIPE_NOALLOC_SCRATCH_BYTES = 128 << 20
 RIPE_ANCHOR_QUERY, RIPE_ANCHOR_CACHE = 0, 1
 RIPE_WINDOW_FULL = 2**31 - 1
 (RIPE_SECTION_LENS, RIPE_SECTION_DEEP_K, RIPE_SECTION_DEEP_V, RIPE_SECTION_RING_K,

@@ -26,6 +26,7 @@
 namespace {
 struct Recorder {
     int appends = 0, verifies = 0, combines = 0;
+    int last_nc = 0, last_pairs = 0;                 // of the last verify launch
     const void* ws = nullptr;        // workspace the test passed
     size_t ws_bytes = 0;
     const void* real = nullptr;      // host memory behind the fake storage
@@ -69,10 +70,25 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t) {
 // partial state of every (sequence, KV head, chunk, row-head) inside the
 // workspace.
 static void check_verify(const VerifyArgs& a, int rt, const char* kind) {
+    rec.last_nc = a.nc;
+    rec.last_pairs = a.n_pairs;
     CHECK(a.rows_here >= 1 && a.rows_here <= kMaxRowsPerLaunch, "%s rows_here %d", kind, a.rows_here);
     CHECK(a.M == a.rows_here * a.group, "%s M %d", kind, a.M);
     CHECK(a.cl >= 32 && a.cl % 32 == 0, "%s chunk length %lld", kind, (long long)a.cl);
-    CHECK(a.n_groups == a.B * a.Hkv * a.nc, "%s n_groups", kind);
+    if (a.n_pairs == 0) {
+        CHECK(a.n_groups == a.B * a.Hkv * a.nc, "%s n_groups", kind);
+    } else {
+        // every (sequence, chunk < its chunk count) exactly once
+        CHECK(a.n_groups == a.n_pairs * a.Hkv && a.n_pairs <= kMaxPairs, "%s pair groups", kind);
+        std::vector<int> seen((size_t)a.B * a.nc, 0);
+        for (int k = 0; k < a.n_pairs; ++k) {
+            const int b = a.pairs[k] & 63, c = a.pairs[k] >> 6;
+            CHECK(b < a.B && c < a.snc[b], "%s pair %d out of range", kind, k);
+            if (b < a.B && c < a.nc) ++seen[(size_t)b * a.nc + c];
+        }
+        for (int b = 0; b < a.B; ++b)
+            for (int c = 0; c < a.snc[b]; ++c) CHECK(seen[(size_t)b * a.nc + c] == 1, "%s pair (%d, %d)", kind, b, c);
+    }
     const int per_item = 16 * rt * (std::strcmp(kind, "rows") == 0 ? 4 : 1);
     CHECK(a.nrb == (a.M + per_item - 1) / per_item, "%s nrb %d", kind, a.nrb);
     for (int k = 1; k < a.rows_here; ++k)
@@ -328,8 +344,33 @@ static void check_workspace_sweep() {
     std::printf("workspace sweep: %ld calls\n", calls);
 }
 
+// A batch whose row blocks fill the chip with one sequence ten times longer
+// than the others: the planner splits it and orders the items longest first.
+static void check_balance_split() {
+    std::mt19937 rng(3);
+    Fake f;
+    CHECK(make(f, config(1, 32, 32, 8, 128, 64, 4, 3008, 8)), "create");
+    CHECK(append_all(f, {3000, 200, 310, 150}) == RIPE_OK, "append");
+    const size_t ws = ripe_workspace_bytes(f.h, 256);
+    CHECK(ws > 0, "no workspace for a call that splits");
+    std::vector<int32_t> blk, loop;
+    for (int r = 1; r <= 32; ++r)
+        for (int i = 0; i < 8; ++i) {
+            blk.push_back(i);
+            loop.push_back(r);
+        }
+    rec.ws = reinterpret_cast<void*>(uintptr_t{1} << 40);
+    rec.ws_bytes = ws;
+    CHECK(ripe_verify_attn(f.h, 0, 256, blk.data(), loop.data(), g_dummy, view(), view(), 8, g_out, g_out,
+                           const_cast<void*>(rec.ws), ws, nullptr) == RIPE_OK, "verify");
+    CHECK(rec.last_nc == 3 && rec.last_pairs == 6, "split into %d chunks, %d items", rec.last_nc, rec.last_pairs);
+    ripe_destroy(f.h);
+    (void)rng;
+}
+
 int main() {
     check_validation();
+    check_balance_split();
     check_workspace_sweep();
     if (rec.failures) {
         std::printf("%d host check(s) failed\n", rec.failures);

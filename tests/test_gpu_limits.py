@@ -87,3 +87,35 @@ def test_long_streams_every_head_size(d, lens):
     KV head with two heads per group."""
     rows = grid_rows(8, 8)                       # 64 rows x 2 query heads per KV head
     run(Workload(f"long{d}", 95 + d, 1, 8, 4, 2, d, 64, 8, lens, 0.88, rows, heavy_frac=0.01))
+
+
+def test_long_sequence_split_for_balance(kernel_choice):
+    """Four sequences whose row blocks alone fill the chip (8 KV heads x 8 row
+    blocks x 4 sequences = 256 workgroups), one of them ten times longer than
+    the others: the planner splits it into chunks no longer than the mean load
+    of a workgroup slot and lists the (sequence, chunk) items longest first.
+    Outputs are compared on a seeded sample of (sequence, row, head), every
+    row of one head of the long sequence included."""
+    import ripe_harness as H
+    wl = Workload("balance", 97, 1, 32, 32, 8, 128, 64, 8, [3000, 200, 310, 150], 0.88, grid_rows(8, 32))
+    cache = H.make_cache(wl)
+    H.load_prefix(cache, wl)
+    if kernel_choice in ("planner", "rows-planner"):
+        assert cache.workspace(wl.n_rows) is not None, "the rows kernel's call may split its keys"
+    q, bk, bv = H.verify_inputs(wl, 0)
+    out, lse = cache.verify(0, wl.rows, q, bk, bv, wl.n_blk)
+    torch.cuda.synchronize()
+    want = np.zeros((wl.batch, wl.n_rows, wl.n_heads_q), dtype=np.uint8)
+    rng = np.random.default_rng(97)
+    want.reshape(-1)[rng.integers(0, want.size, size=200)] = 1
+    want[0, :, 3] = 1
+    want[:, -1, :] = 1
+    oc = oracle.prefix_cache(wl, layers=[0])
+    ref_o, ref_l = oc.verify(0, wl.rows, wl.queries(0), *wl.block(0), wl.n_blk, want=want)
+    sel = want.astype(bool)
+    o = out.cpu().double().numpy()[sel]
+    l = lse.cpu().double().numpy()[sel]
+    err_o = float(np.max(np.abs(o - ref_o[sel])))
+    err_l = float(np.max(np.abs(l - ref_l[sel]) / np.maximum(1.0, np.abs(ref_l[sel]))))
+    print(f"balance split: {int(sel.sum())} outputs, max|dO|={err_o:.3e} rel dLSE={err_l:.3e}", flush=True)
+    assert err_o <= TOL_O and err_l <= TOL_LSE
