@@ -303,6 +303,38 @@ def test_p7_single_key():
         np.testing.assert_array_equal(out[0, kk, 0], v)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(6, 3), (8, 2), (4, 4), (5, 1)])
+def test_p7_gqa_head_mapping(Hq, Hkv):
+    """Zero keys (uniform softmax) and every value of KV head g equal to g + 1
+    in dimension 0 (zero elsewhere), at every plane and in the draft block:
+    query head h must return exactly floor(h * Hkv / Hq) + 1, i.e. contiguous
+    groups of Hq / Hkv query heads per KV head (reading R6)."""
+    L, R, W, D, d = 9, 3, 4, 2, 32
+    cfg = oracle.config(1, R, Hq, Hkv, d, W, 1, L + D, D)
+    oc = oracle.OracleCache(cfg)
+    nw = min(L, W)
+    dk = np.zeros((1, Hkv, L, d), np.uint16)
+    dv = np.zeros_like(dk)
+    wk = np.zeros((1, R - 1, Hkv, nw, d), np.uint16)
+    wv = np.zeros_like(wk)
+    bk = np.zeros((1, R, Hkv, D, d), np.uint16)
+    bv = np.zeros_like(bk)
+    for g in range(Hkv):
+        tag = f32_to_bf16(np.array([g + 1.0], np.float32))[0]
+        dv[0, g, :, 0] = tag
+        wv[0, :, g, :, 0] = tag
+        bv[0, :, g, :, 0] = tag
+    assert oc.append(0, [L], dk, dv, wk, wv) == oracle.ORA_OK
+    rows = grid_rows(D, R)
+    q = f32_to_bf16(np.random.default_rng(11).standard_normal((1, len(rows), Hq, d)).astype(np.float32))
+    out, lse = oc.verify(0, rows, q, bk, bv, D)
+    for kk, (i, r) in enumerate(rows):
+        for h in range(Hq):
+            assert abs(out[0, kk, h, 0] - ((h * Hkv) // Hq + 1)) < 1e-12
+            assert not np.any(out[0, kk, h, 1:])
+            assert abs(lse[0, kk, h] - math.log(L + i + 1)) < 1e-12
+
+
 # ---------------------------------------------------------------- P9 and errors
 
 def _golden(name):
@@ -321,6 +353,11 @@ def test_p9_memory_fraction_matches_page():
     # at R = 32 loops and 4 single-plane layers outside the recurrence.
     f = ripe_fraction(int(g["context"]), int(g["window"]), 32, n_recurrent=4, n_plain=4)
     assert abs(100 * f - g["fraction_percent"]) <= g["print_precision_percent"]
+    # without that assumption (recurrent layers only) the same closed form
+    # gives 9.18%: the page's figure pins the formula only together with the
+    # assumed layer split, so P9 is a consistency check
+    f0 = ripe_fraction(int(g["context"]), int(g["window"]), 32, n_recurrent=4, n_plain=0)
+    assert abs(100 * f0 - 9.18) < 0.01
     # the stored vectors of the byte layout agree with the closed form
     wl = tiny([40], 5, 1, 1, 1, 7, n_layers=1)
     oc, brutes = build_both(wl, n_steps=3)
