@@ -519,27 +519,63 @@ __device__ inline int wave_max(int x) { return wave_reduce<true>(x); }
 __device__ inline void dma16(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(lds) : "memory");
 }
-// 4 bytes per lane (lane l lands at lds + 4 l); same contract as dma16
-__device__ inline void dma4(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" :: "v"(g), "s"(lds) : "memory");
-}
 __device__ inline uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-// load_stage through dma16
+// N consecutive 1 KB blocks by direct loads: block i from sbase + voff +
+// 1 KB i into lds + 1 KB i + 16 lane (the instruction offset moves the global
+// and the LDS address alike).  sbase is wave-uniform (scalar registers), so a
+// run costs one scalar move besides its N loads; same contract as dma16.
+template <int N>
+__device__ inline void dma16_run(const void* sbase, uint32_t voff, uint32_t lds) {
+    static_assert(N >= 2 && N <= 4, "two to four blocks");
+    if constexpr (N == 4)
+        asm volatile("s_mov_b32 m0, %2\n\t"
+                     "global_load_lds_dwordx4 %0, %1\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:2048\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:3072" :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+    else if constexpr (N == 3)
+        asm volatile("s_mov_b32 m0, %2\n\t"
+                     "global_load_lds_dwordx4 %0, %1\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:2048" :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\t"
+                     "global_load_lds_dwordx4 %0, %1\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:1024" :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+// N 4-byte loads (lane l of load i: sbase + 4 l + 256 i into lds + 256 i + 4 l)
+template <int N>
+__device__ inline void dma4_run(const void* sbase, uint32_t lds, int lane) {
+    static_assert(N >= 2 && N <= 4, "two to four loads");
+    const uint32_t voff = 4 * lane;
+    if constexpr (N == 4)
+        asm volatile("s_mov_b32 m0, %2\n\t"
+                     "global_load_lds_dword %0, %1\n\t"
+                     "global_load_lds_dword %0, %1 offset:256\n\t"
+                     "global_load_lds_dword %0, %1 offset:512\n\t"
+                     "global_load_lds_dword %0, %1 offset:768" :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+    else if constexpr (N == 3)
+        asm volatile("s_mov_b32 m0, %2\n\t"
+                     "global_load_lds_dword %0, %1\n\t"
+                     "global_load_lds_dword %0, %1 offset:256\n\t"
+                     "global_load_lds_dword %0, %1 offset:512" :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\t"
+                     "global_load_lds_dword %0, %1\n\t"
+                     "global_load_lds_dword %0, %1 offset:256" :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+// A staged tile pair is D/8 blocks of 1 KB (the key tile's D/16, then the
+// value tile's), block b at stage + 1 KB b.  Wave w of the four loading it
+// takes the D/32 consecutive blocks from D/32 * w on: waves 0 and 1 the key
+// tile, 2 and 3 the value tile.  Its first block within that tile, and the
+// lane's 16 bytes in a block (a storage block is the operand piece order of
+// the instruction: lane l reads row l % 16, dims 8 (l / 16)..+8), as a byte
+// offset from the tile:
 template <int D>
-__device__ inline void load_stage_asm(const uint16_t* Kt, const uint16_t* Vt, uint16_t* stage, int wave,
-                                      int lane) {
-    constexpr int BLOCKS = D / 8;
-    static_assert(BLOCKS % 4 == 0, "four waves share the blocks");
-    const int src_off = (lane & 15) * 32 + (lane >> 4) * 8;
-    const uint32_t base = lds_addr(stage);
-#pragma unroll
-    for (int j = 0; j < BLOCKS / 4; ++j) {
-        const int blk = j * 4 + wave;
-        const uint16_t* src = (blk < BLOCKS / 2 ? Kt + blk * 512 : Vt + (blk - BLOCKS / 2) * 512) + src_off;
-        dma16(src, base + blk * 1024);
-    }
+__device__ inline uint32_t stage_lane_offset(int wave, int lane) {
+    return (uint32_t)(((wave & 1) * (D / 32)) * 1024 + ((lane & 15) * 32 + (lane >> 4) * 8) * 2);
 }
 // The operand pieces of a staged tile pair as ordinary LDS loads (piece i at
 // stage + 1 KB * i, this lane's 16 bytes at + 16 lane): the key half and the
@@ -958,26 +994,29 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
         }
     }
 
-    // issue cursor: the j-th issue of this wave loads tile 2j + kh of the stream
+    // issue cursor: the j-th issue of this wave loads tile 2j + kh of the
+    // stream; this wave's blocks of it are in the key tile (rw < 2) or the
+    // value tile, at iKV (deep tiles), from stage + 1 KB * PT * rw
     int ti = kh, ipl = 0, ist = 0;
-    const uint16_t* iK = gK + (int64_t)(d0 + 32 * kh) * D;
-    const uint16_t* iV = gV + (int64_t)(d0 + 32 * kh) * D;
+    const uint16_t* iKV = (rw < 2 ? gK : gV) + (int64_t)(d0 + 32 * kh) * D;
+    const uint32_t voff = stage_lane_offset<D>(rw, lane);
+    const uint16_t* ring_kv = rw < 2 ? a.ring_k : a.ring_v;
     int issued = 0;                               // tile pairs issued by this wave
     auto issue_next = [&](uint16_t* stage) {
+        const uint32_t l = lds_addr(stage) + rw * PT * 1024;
         if (PRIV || ti < n_deep) {                // with private waves the stream is deep only
-            load_stage_asm<D>(iK, iV, stage, rw, lane);
+            dma16_run<PT>(iKV, voff, l);
         } else {
             if (ti - 2 < n_deep) { ipl = 0; ist = ti - n_deep; }   // first ring tile of this half
             while (ist >= ring_tiles) { ist -= ring_tiles; ++ipl; }
             const int r = ipl < 64 ? __builtin_amdgcn_readlane(loops_v0, ipl)
                                    : __builtin_amdgcn_readlane(loops_v1, ipl - 64);
             const int64_t off = rreg0 + (int64_t)(r - 1) * WPD + (int64_t)ist * TILE;
-            load_stage_asm<D>(a.ring_k + off, a.ring_v + off, stage, rw, lane);
+            dma16_run<PT>(ring_kv + off, voff, l);
             ist += 2;
         }
         ti += 2;
-        iK += 2 * TILE;
-        iV += 2 * TILE;
+        iKV += 2 * TILE;
         ++issued;
     };
     // Past the end of its tiles a wave still issues one group of PT loads per
@@ -989,9 +1028,7 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
     // waits keep the loop free of branches the compiler would thread across
     // its back edge.
     auto issue_dummy = [&](uint16_t* stage) {
-        const uint32_t l = lds_addr(stage);
-#pragma unroll
-        for (int k = 0; k < PT; ++k) dma4(gK + 2 * lane, l + 256 * k);
+        dma4_run<PT>(gK, lds_addr(stage), lane);  // (the first 1 KB of the plane)
         ti += 2;
         ++issued;
     };
