@@ -121,6 +121,8 @@ __device__ inline float max_lane_groups(float x) {
 // maximum grows.  O = sum p v / l and LSE = (m + log2 l) ln 2 hold for any
 // reference, and fp32 keeps l and O exact enough at that scale.
 constexpr float kLazyLog2 = 8.f;
+constexpr float kLazyMax = 256.f;       // 2^kLazyLog2
+static_assert(kLazyMax == (float)(1 << (int)kLazyLog2), "the margin and its power of two");
 
 // Moves the references that the tile maximum bm passes by more than the margin
 // (bm = -inf never does) and rescales l and O there by 2^(m_old - m_new): 0 on
@@ -141,18 +143,11 @@ __device__ inline void lazy_rescale(RowTile<D>& rt, float bm) {
     }
 }
 
-// p = 2^(s c - m) of a lane's 8 raw scores s against the finite reference m
-// (one fma per score), added to l, and O += P V with P split into bf16
+// A lane's 8 weights p added to l, and O += P V with P split into bf16
 // hi = round(p) and lo = round(p - hi)
 template <int D>
-__device__ inline void accumulate(RowTile<D>& rt, const Frags<D>& f, const float (&x)[8], float c, float m) {
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -m));
-    float ps = p[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) ps += p[e];
-    rt.l += ps;
+__device__ inline void accumulate_p(RowTile<D>& rt, const Frags<D>& f, const float (&p)[8]) {
+    rt.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
@@ -166,6 +161,15 @@ __device__ inline void accumulate(RowTile<D>& rt, const Frags<D>& f, const float
     for (int dt = 0; dt < D / 16; ++dt) rt.o[dt] = mfma(f.v[dt], phi, rt.o[dt]);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) rt.o[dt] = mfma(f.v[dt], plo, rt.o[dt]);
+}
+// p = 2^(s c - m) of a lane's 8 raw scores s against the finite reference m
+// (one fma per score), then accumulate_p
+template <int D>
+__device__ inline void accumulate(RowTile<D>& rt, const Frags<D>& f, const float (&x)[8], float c, float m) {
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -m));
+    accumulate_p<D>(rt, f, p);
 }
 
 // S^T = K.Q^T of one key tile against one row tile: lane n, register e holds
@@ -187,6 +191,19 @@ __device__ inline float tile_scores(const RowTile<D>& rt, const Frags<D>& f, flo
     x[4] = s1[0]; x[5] = s1[1]; x[6] = s1[2]; x[7] = s1[3];
     return max8(x);
 }
+// the raw scores alone, for a caller whose first reader of them follows in
+// the same block (no branch between the matrix instructions and that read)
+template <int D>
+__device__ inline void scores_raw(const RowTile<D>& rt, const Frags<D>& f, float (&x)[8]) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+        s0 = mfma(f.k[k][0], rt.q[k], s0);
+        s1 = mfma(f.k[k][1], rt.q[k], s1);
+    }
+    x[0] = s0[0]; x[1] = s0[1]; x[2] = s0[2]; x[3] = s0[3];
+    x[4] = s1[0]; x[5] = s1[1]; x[6] = s1[2]; x[7] = s1[3];
+}
 
 // The rest of a tile for a key tile every row-head of the row tile reads in
 // full: no masks, every score finite (so every reference is finite after the
@@ -199,24 +216,30 @@ __device__ inline void tile_finish_full(RowTile<D>& rt, const Frags<D>& f, const
     accumulate<D>(rt, f, x, c, rt.m);
 }
 
-// tile_finish_full for all row tiles of a wave at once: one rescale test for
-// all of them, then every tile's exponentials and matrix products in one
-// block, so the products of one row tile can run beside the exponentials of
-// the next.
+// The fast-phase tile step of the rows kernel for all row tiles of a wave
+// (every key valid for every row-head, every score finite).  The weights are
+// first taken against the current references; only when one of them passes
+// 2^kLazyLog2 (a row-head's first tile, or a tile whose maximum passes the
+// reference by more than the margin) are the row-heads' maxima formed across
+// their four lane groups, the references moved, l and O rescaled and the
+// weights taken again.  The common test reads only the lane's own weights.
 template <int D, int RT>
-__device__ inline void tiles_finish_full(RowTile<D> (&rt)[RT], const Frags<D>& f, const float (&x)[RT][8],
-                                         const float (&bx)[RT], float c) {
-    float bm[RT];
-    bool up[RT], any = false;
+__device__ inline void tiles_fast(RowTile<D> (&rt)[RT], const Frags<D>& f, const float (&x)[RT][8], float c) {
+    float p[RT][8];
 #pragma unroll
-    for (int tr = 0; tr < RT; ++tr) {
-        bm[tr] = max_lane_groups(bx[tr]) * c;
-        up[tr] = bm[tr] - rt[tr].m > kLazyLog2;
-        any = any || up[tr];
-    }
-    if (__any(any)) {
+    for (int tr = 0; tr < RT; ++tr)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[tr][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[tr][e], c, -rt[tr].m));
+    float pm = max8(p[0]);
+#pragma unroll
+    for (int tr = 1; tr < RT; ++tr) pm = fmaxp(pm, max8(p[tr]));
+    if (__any(pm > kLazyMax)) {
+        float bm[RT];
+        bool up[RT];
 #pragma unroll
         for (int tr = 0; tr < RT; ++tr) {
+            bm[tr] = max_lane_groups(max8(x[tr])) * c;
+            up[tr] = bm[tr] - rt[tr].m > kLazyLog2;
             const float mo = rt[tr].m;
             const float alpha = up[tr] ? __builtin_amdgcn_exp2f(mo - bm[tr]) : 1.f;
             rt[tr].m = up[tr] ? bm[tr] : mo;
@@ -226,10 +249,12 @@ __device__ inline void tiles_finish_full(RowTile<D> (&rt)[RT], const Frags<D>& f
                 rt[tr].o[dt][0] *= alpha; rt[tr].o[dt][1] *= alpha;
                 rt[tr].o[dt][2] *= alpha; rt[tr].o[dt][3] *= alpha;
             }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[tr][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[tr][e], c, -rt[tr].m));
         }
     }
 #pragma unroll
-    for (int tr = 0; tr < RT; ++tr) accumulate<D>(rt[tr], f, x[tr], c, rt[tr].m);
+    for (int tr = 0; tr < RT; ++tr) accumulate_p<D>(rt[tr], f, p[tr]);
 }
 
 // the rest of a tile with masks (invalid keys get -inf; a row-head that has
@@ -1149,15 +1174,21 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
             sn = sn == S - 1 ? 0 : sn + 1;
         }
     }
-    // fast phase: every row-head reads both tiles of the iteration in full
+    // fast phase: every row-head reads both tiles of the iteration in full.
+    // The next tile's operands are read without a test (past this half's
+    // last tile the stage holds whatever its dummy loads bring, and no step
+    // uses those operands), so the step from the scores' matrix instructions
+    // to their first reader is one block.
     for (; j < n_fast; ++j) {
         advance(j);
-        float x[RTW][8], bx[RTW];
+        float x[RTW][8];
 #pragma unroll
-        for (int tr = 0; tr < RTW; ++tr) bx[tr] = tile_scores<D>(rt[tr], f, x[tr]);
-        next_keys(j);
-        tiles_finish_full<D, RTW>(rt, f, x, bx, sl2);
-        next_values(j);
+        for (int tr = 0; tr < RTW; ++tr) scores_raw<D>(rt[tr], f, x[tr]);
+        lds_keys<D>(s_tile[sn][kh], f, lane);
+        tiles_fast<D, RTW>(rt, f, x, sl2);
+        lds_values<D>(s_tile[sn][kh], f, lane);
+        sj = sn;
+        sn = sn == S - 1 ? 0 : sn + 1;
     }
     // general phase: deep tiles with masks, then ring tiles
     int cpl = 0, cst = 0;                         // ring cursor of the compute side
