@@ -224,16 +224,17 @@ __device__ inline void tile_finish_full(RowTile<D>& rt, const Frags<D>& f, const
 // their four lane groups, the references moved, l and O rescaled and the
 // weights taken again.  The common test reads only the lane's own weights.
 template <int D, int RT>
-__device__ inline void tiles_fast(RowTile<D> (&rt)[RT], const Frags<D>& f, const float (&x)[RT][8], float c) {
+__device__ inline void tiles_fast(RowTile<D> (&rt)[RT], const Frags<D>& f, const float (&x)[RT][8],
+                                  const float (&bx)[RT], float c) {
     float p[RT][8];
 #pragma unroll
     for (int tr = 0; tr < RT; ++tr)
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[tr][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[tr][e], c, -rt[tr].m));
-    float pm = max8(p[0]);
+    bool over = false;
 #pragma unroll
-    for (int tr = 1; tr < RT; ++tr) pm = fmaxp(pm, max8(p[tr]));
-    if (__any(pm > kLazyMax)) {
+    for (int tr = 0; tr < RT; ++tr) over = over || __builtin_fmaf(bx[tr], c, -rt[tr].m) > kLazyLog2;
+    if (__any(over)) {
         float bm[RT];
         bool up[RT];
 #pragma unroll
@@ -1180,12 +1181,24 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
     // uses those operands), so the step from the scores' matrix instructions
     // to their first reader is one block.
     for (; j < n_fast; ++j) {
-        advance(j);
-        float x[RTW][8];
+        const bool bar = K == 1 || j % K == 0;
+        if (bar) {
+            __builtin_amdgcn_s_waitcnt(0x070 | ((P - 1 - K) * PT));
+            asm volatile("s_barrier" ::: "memory");
+        }
+        float x[RTW][8], bx[RTW];
 #pragma unroll
-        for (int tr = 0; tr < RTW; ++tr) scores_raw<D>(rt[tr], f, x[tr]);
+        for (int tr = 0; tr < RTW; ++tr) bx[tr] = tile_scores<D>(rt[tr], f, x[tr]);
+        if (bar) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int st = (sj + P + k) % S;
+                if (ti < n_tiles) issue_next(s_tile[st][kh]);
+                else issue_dummy(s_tile[st][kh]);
+            }
+        }
         lds_keys<D>(s_tile[sn][kh], f, lane);
-        tiles_fast<D, RTW>(rt, f, x, sl2);
+        tiles_fast<D, RTW>(rt, f, x, bx, sl2);
         lds_values<D>(s_tile[sn][kh], f, lane);
         sj = sn;
         sn = sn == S - 1 ? 0 : sn + 1;
