@@ -191,20 +191,6 @@ __device__ inline float tile_scores(const RowTile<D>& rt, const Frags<D>& f, flo
     x[4] = s1[0]; x[5] = s1[1]; x[6] = s1[2]; x[7] = s1[3];
     return max8(x);
 }
-// the raw scores alone, for a caller whose first reader of them follows in
-// the same block (no branch between the matrix instructions and that read)
-template <int D>
-__device__ inline void scores_raw(const RowTile<D>& rt, const Frags<D>& f, float (&x)[8]) {
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < D / 32; ++k) {
-        s0 = mfma(f.k[k][0], rt.q[k], s0);
-        s1 = mfma(f.k[k][1], rt.q[k], s1);
-    }
-    x[0] = s0[0]; x[1] = s0[1]; x[2] = s0[2]; x[3] = s0[3];
-    x[4] = s1[0]; x[5] = s1[1]; x[6] = s1[2]; x[7] = s1[3];
-}
-
 // The rest of a tile for a key tile every row-head of the row tile reads in
 // full: no masks, every score finite (so every reference is finite after the
 // rescale).  bx: the lane's score maximum from tile_scores.  Uses only f.v.
@@ -492,27 +478,6 @@ __device__ inline void sum_lane_groups(RowTile<D>& rt) {
 }
 
 // ---------------------------------------------------------------- many rows
-
-// Issue the global->LDS loads of one K+V tile pair into an LDS stage.  The
-// pair is D/8 blocks of 1 KB (D/16 of K, then D/16 of V); this thread's wave
-// loads blocks j*4 + wave (j < D/32).  Within a block, lane l loads the 16 bytes the
-// matrix operand wants in lane l (key or value row l%16, columns 8*(l/16)..),
-// which the LDS write puts at l*16.
-template <int D>
-__device__ inline void load_stage(const uint16_t* Kt, const uint16_t* Vt, uint16_t* stage, int wave,
-                                  int lane) {
-    constexpr int BLOCKS = D / 8;                     // 1 KB blocks in a K+V pair
-    static_assert(BLOCKS % 4 == 0, "four waves share the blocks");
-    const int src_off = (lane & 15) * 32 + (lane >> 4) * 8;
-#pragma unroll
-    for (int j = 0; j < BLOCKS / 4; ++j) {
-        const int blk = j * 4 + wave;
-        const uint16_t* src = (blk < BLOCKS / 2 ? Kt + blk * 512 : Vt + (blk - BLOCKS / 2) * 512) + src_off;
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                         (void __attribute__((address_space(3)))*)(stage + blk * 512),
-                                         16, 0, 0);
-    }
-}
 
 // Workgroup barrier that waits for this wave's LDS operations but leaves its
 // global loads in flight (no memory fence, so no vmcnt(0)); the memory clobber
