@@ -1031,6 +1031,7 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
         if (ti < n_tiles) issue_next(s_tile[j][kh]);
         else issue_dummy(s_tile[j][kh]);
     }
+    int si = P % S;                               // stage of the next issue (tile m in stage m mod S)
 
     // this wave's loops (ascending, at most two on the fast path) with their
     // largest block offsets, from the sorted row words
@@ -1117,9 +1118,9 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
         // P + j .. P + j + K - 1, replace tiles consumed by now
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const int st = (sj + P + k) % S;       // sj = j mod S
-            if (ti < n_tiles) issue_next(s_tile[st][kh]);
-            else issue_dummy(s_tile[st][kh]);
+            if (ti < n_tiles) issue_next(s_tile[si][kh]);
+            else issue_dummy(s_tile[si][kh]);
+            si = si == S - 1 ? 0 : si + 1;
         }
     };
     auto next_keys = [&](int j) {
@@ -1145,7 +1146,14 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
     // last tile the stage holds whatever its dummy loads bring, and no step
     // uses those operands), so the step from the scores' matrix instructions
     // to their first reader is one block.
-    for (; j < n_fast; ++j) {
+    // The fast steps whose issues are all deep tiles of the stream (every
+    // step before the last few of a long chunk) issue them without the tests
+    // of issue_next: j < n_fd, a whole number of barrier groups.  The split
+    // point may differ between the halves; both loops pass the same barriers.
+    const int n_sdeep = PRIV ? n_tiles : n_deep;  // deep tiles of the stream
+    int n_fd = min(n_fast, (n_sdeep - kh + 1) / 2 - P);
+    n_fd = n_fd < 0 ? 0 : n_fd / K * K;
+    auto fast_step = [&](int j, bool deep_issue) {
         const bool bar = K == 1 || j % K == 0;
         if (bar) {
             __builtin_amdgcn_s_waitcnt(0x070 | ((P - 1 - K) * PT));
@@ -1157,9 +1165,17 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
         if (bar) {
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const int st = (sj + P + k) % S;
-                if (ti < n_tiles) issue_next(s_tile[st][kh]);
-                else issue_dummy(s_tile[st][kh]);
+                if (deep_issue) {
+                    dma16_run<PT>(iKV, voff, lds_addr(s_tile[si][kh]) + rw * PT * 1024);
+                    ti += 2;
+                    iKV += 2 * TILE;
+                    ++issued;
+                } else if (ti < n_tiles) {
+                    issue_next(s_tile[si][kh]);
+                } else {
+                    issue_dummy(s_tile[si][kh]);
+                }
+                si = si == S - 1 ? 0 : si + 1;
             }
         }
         lds_keys<D>(s_tile[sn][kh], f, lane);
@@ -1167,7 +1183,9 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
         lds_values<D>(s_tile[sn][kh], f, lane);
         sj = sn;
         sn = sn == S - 1 ? 0 : sn + 1;
-    }
+    };
+    for (; j < n_fd; ++j) fast_step(j, true);
+    for (; j < n_fast; ++j) fast_step(j, false);
     // general phase: deep tiles with masks, then ring tiles
     int cpl = 0, cst = 0;                         // ring cursor of the compute side
     for (; j < n_iter; ++j) {
