@@ -519,8 +519,11 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // run costs one scalar move besides its N loads; same contract as dma16.
 template <int N>
 __device__ inline void dma16_run(const void* sbase, uint32_t voff, uint32_t lds) {
-    static_assert(N >= 2 && N <= 4, "two to four blocks");
-    if constexpr (N == 4)
+    static_assert(N >= 1 && N <= 4, "one to four blocks");
+    if constexpr (N == 1)
+        asm volatile("s_mov_b32 m0, %2\n\t"
+                     "global_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+    else if constexpr (N == 4)
         asm volatile("s_mov_b32 m0, %2\n\t"
                      "global_load_lds_dwordx4 %0, %1\n\t"
                      "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
@@ -1162,10 +1165,15 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
         float x[RTW][8], bx[RTW];
 #pragma unroll
         for (int tr = 0; tr < RTW; ++tr) bx[tr] = tile_scores<D>(rt[tr], f, x[tr]);
+        // (K = 1, deep issue: half the run now, half after the exponentials)
+        constexpr bool kSplitRun = K == 1 && PT % 2 == 0;
+        const uint32_t l_run = lds_addr(s_tile[si][kh]) + rw * PT * 1024;
         if (bar) {
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                if (deep_issue) {
+                if (deep_issue && kSplitRun) {
+                    dma16_run<PT / 2>(iKV, voff, l_run);
+                } else if (deep_issue) {
                     dma16_run<PT>(iKV, voff, lds_addr(s_tile[si][kh]) + rw * PT * 1024);
                     ti += 2;
                     iKV += 2 * TILE;
@@ -1180,6 +1188,12 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
         }
         lds_keys<D>(s_tile[sn][kh], f, lane);
         tiles_fast<D, RTW>(rt, f, x, bx, sl2);
+        if (deep_issue && kSplitRun) {
+            dma16_run<PT / 2>(iKV + PT / 2 * 512, voff, l_run + PT / 2 * 1024);
+            ti += 2;
+            iKV += 2 * TILE;
+            ++issued;
+        }
         lds_values<D>(s_tile[sn][kh], f, lane);
         sj = sn;
         sn = sn == S - 1 ? 0 : sn + 1;
