@@ -453,10 +453,13 @@ __device__ inline void write_result_word(const VerifyArgs& a, const Item& it, co
     if (it.nc_b == 1) {
         const float inv = 1.f / rt.l;
         float* op = a.out + (((int64_t)it.b * a.n_rows + orig) * a.Hq + h) * D;
+        // final rows are not read again by this call: non-temporal stores,
+        // so they do not wait in L2 for the write-back at the kernel's end
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
-            *reinterpret_cast<float4*>(op + dt * 16 + 4 * q) =
-                make_float4(rt.o[dt][0] * inv, rt.o[dt][1] * inv, rt.o[dt][2] * inv, rt.o[dt][3] * inv);
+            __builtin_nontemporal_store(f32x4{rt.o[dt][0] * inv, rt.o[dt][1] * inv, rt.o[dt][2] * inv,
+                                              rt.o[dt][3] * inv},
+                                        reinterpret_cast<f32x4*>(op + dt * 16 + 4 * q));
         if (q == 0)
             a.lse[((int64_t)it.b * a.n_rows + orig) * a.Hq + h] = (rt.m + log2f(rt.l)) * kLn2;
     } else {
@@ -1719,7 +1722,7 @@ __global__ void __launch_bounds__(256) k_combine(VerifyArgs a) {
 #pragma unroll
     for (int t = 0; t < NE; ++t) {
         const int e = lane + 64 * t;
-        if (e < D) op[e] = acc[t] * inv;
+        if (e < D) __builtin_nontemporal_store(acc[t] * inv, op + e);   // (final rows, as above)
     }
     if (lane == 0) a.lse[((int64_t)b * a.n_rows + orig) * a.Hq + h] = (mx + log2f(lt)) * kLn2;
 }
