@@ -384,6 +384,10 @@ ripe_status attend(ripe_cache* cache, int32_t layer, int32_t n_rows, const int32
         for (int b = 0; b < kMaxSeqArgs; ++b)
             a.snc[b] = b < g.B ? (lens[b] > 0 ? (int32_t)((lens[b] + p.cx + p.cl - 1) / p.cl) : 1) : 0;
         order_pairs(a, lens, g.B);
+        a.n_split = 0;
+        if (p.nc > 1 && g.B <= kMaxSeqArgs)
+            for (int b = 0; b < g.B; ++b)
+                if (a.snc[b] > 1) a.split_b[a.n_split++] = (uint8_t)b;
         const hipError_t e = p.rows_kernel ? launch_verify_rows(a, p.rt, p.priv, stream)
                                            : launch_verify_keys(a, p.rt, p.wide, stream);
         if (e != hipSuccess) return RIPE_EDEVICE;

@@ -84,6 +84,11 @@ struct VerifyArgs {
     // first (bits 0..5 sequence, 6..15 chunk), so the longest start first
     int32_t n_pairs;
     uint16_t pairs[kMaxPairs];
+    // for the combine launch: the sequences split into two or more chunks
+    // when the batch has at most kMaxSeqArgs sequences (n_split = 0: every
+    // sequence is enumerated and the unsplit ones skipped)
+    int32_t n_split;
+    uint8_t split_b[kMaxSeqArgs];
 };
 
 // matrix-core kernels: "keys" (waves split the key tiles of 16*rt row-heads)

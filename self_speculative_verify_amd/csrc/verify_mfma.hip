@@ -1636,11 +1636,13 @@ template <int D>
 __global__ void __launch_bounds__(256) k_combine(VerifyArgs a) {
     const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int64_t total = (int64_t)a.B * a.Hkv * a.M;
+    // row-heads of the split sequences only, where the launch lists them
+    const int64_t total = (int64_t)(a.n_split > 0 ? a.n_split : a.B) * a.Hkv * a.M;
     if (idx >= total) return;
     const int u = (int)(idx % a.M);
-    const int bg = (int)(idx / a.M);
-    const int g = bg % a.Hkv, b = bg / a.Hkv;
+    const int sg = (int)(idx / a.M);
+    const int g = sg % a.Hkv, b = a.n_split > 0 ? (int)a.split_b[sg / a.Hkv] : sg / a.Hkv;
+    const int bg = b * a.Hkv + g;
     int nc_b = b < kMaxSeqArgs ? a.snc[b] : 0;
     if (nc_b == 0) {
         const int64_t L = a.lens[b];
@@ -1785,7 +1787,7 @@ hipError_t launch_verify_rows(const VerifyArgs& a, int rtw, bool priv, hipStream
 }
 
 hipError_t launch_combine(const VerifyArgs& a, hipStream_t s) {
-    const int64_t units = (int64_t)a.B * a.Hkv * a.M;
+    const int64_t units = (int64_t)(a.n_split > 0 ? a.n_split : a.B) * a.Hkv * a.M;
     const unsigned blocks = (unsigned)((units + 3) / 4);
     if (blocks == 0) return hipSuccess;
     switch (a.d) {

@@ -125,6 +125,19 @@ hipError_t launch_verify_rows(const VerifyArgs& a, int rt, bool priv, hipStream_
 hipError_t launch_combine(const VerifyArgs& a, hipStream_t) {
     ++rec.combines;
     CHECK(a.nc > 1, "combine of a single chunk");
+    // the combine's sequence list: every split sequence once, ascending, or
+    // none (every sequence enumerated) for larger batches
+    if (a.B > kMaxSeqArgs) {
+        CHECK(a.n_split == 0, "combine list for %d sequences", a.B);
+    } else {
+        int k = 0;
+        for (int b = 0; b < a.B; ++b)
+            if (a.snc[b] > 1) {
+                CHECK(k < a.n_split && a.split_b[k] == b, "combine list misses sequence %d", b);
+                ++k;
+            }
+        CHECK(k == a.n_split && k > 0, "combine list of %d sequences, %d split", a.n_split, k);
+    }
     return hipSuccess;
 }
 
