@@ -998,7 +998,6 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
     const uint16_t* iKV = (rw < 2 ? gK : gV) + (int64_t)(d0 + 32 * kh) * D;
     const uint32_t voff = stage_lane_offset<D>(rw, lane);
     const uint16_t* ring_kv = rw < 2 ? a.ring_k : a.ring_v;
-    int issued = 0;                               // tile pairs issued by this wave
     auto issue_next = [&](uint16_t* stage) {
         const uint32_t l = lds_addr(stage) + rw * PT * 1024;
         if (PRIV || ti < n_deep) {                // with private waves the stream is deep only
@@ -1014,7 +1013,6 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
         }
         ti += 2;
         iKV += 2 * TILE;
-        ++issued;
     };
     // Past the end of its tiles a wave still issues one group of PT loads per
     // step: PT 4-byte loads of valid memory into the stage the missing tile
@@ -1027,7 +1025,6 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
     auto issue_dummy = [&](uint16_t* stage) {
         dma4_run<PT>(gK, lds_addr(stage), lane);  // (the first 1 KB of the plane)
         ti += 2;
-        ++issued;
     };
     static_assert((P - 1) * PT <= 15, "vmcnt field");
 
@@ -1176,12 +1173,11 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
             for (int k = 0; k < K; ++k) {
                 if (deep_issue && kSplitRun) {
                     dma16_run<PT / 2>(iKV, voff, l_run);
-                } else if (deep_issue) {
+                } else if (deep_issue) {              // (si moves with k)
                     dma16_run<PT>(iKV, voff, lds_addr(s_tile[si][kh]) + rw * PT * 1024);
                     ti += 2;
                     iKV += 2 * TILE;
-                    ++issued;
-                } else if (ti < n_tiles) {
+                            } else if (ti < n_tiles) {
                     issue_next(s_tile[si][kh]);
                 } else {
                     issue_dummy(s_tile[si][kh]);
@@ -1195,8 +1191,7 @@ __global__ void __launch_bounds__(PRIV ? 768 : 512, 1) k_verify_rows(VerifyArgs 
             dma16_run<PT / 2>(iKV + PT / 2 * 512, voff, l_run + PT / 2 * 1024);
             ti += 2;
             iKV += 2 * TILE;
-            ++issued;
-        }
+            }
         lds_values<D>(s_tile[sn][kh], f, lane);
         sj = sn;
         sn = sn == S - 1 ? 0 : sn + 1;
