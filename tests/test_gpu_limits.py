@@ -28,7 +28,8 @@ def _gpu():
     yield
 
 
-@pytest.fixture(params=["planner", "keys-4waves", "keys-8waves-planner", "rows-planner", "keys-chunked"],
+@pytest.fixture(params=["planner", "keys-4waves", "keys-8waves-planner", "rows-planner", "keys-chunked",
+                        "rows-chunked"],
                 autouse=True)
 def kernel_choice(request, monkeypatch):
     use_tuning(monkeypatch, request.param)
