@@ -149,6 +149,20 @@ ripe_status ripe_cache_create(const ripe_config* cfg, void* d_storage, size_t by
                               hipStream_t stream, ripe_cache** out);
 
 /*
+ * Bind a handle to storage that already holds a cache image of the same
+ * configuration (for example a checkpoint of another handle's storage copied
+ * back into device memory): nothing is written, and the committed lengths are
+ * read from the image's lengths section on `stream` (the call waits for that
+ * copy).  Appends and verifies then continue from the image exactly as they
+ * would have on the handle that wrote it.  RIPE_EINVAL, with *out NULL, for
+ * an invalid configuration or storage, or for a stored length outside
+ * [0, capacity]; RIPE_EDEVICE if the copy fails.  No page defines the call
+ * (checkpoint and resume of the cache are this library's).
+ */
+ripe_status ripe_cache_open(const ripe_config* cfg, void* d_storage, size_t bytes,
+                            hipStream_t stream, ripe_cache** out);
+
+/*
  * Release the handle (host memory only; the storage stays the caller's).
  * NULL is accepted, and so is a handle that was already destroyed: the
  * library keeps a registry of live handles and ignores any other pointer (a

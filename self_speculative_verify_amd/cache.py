@@ -26,7 +26,9 @@ class RipeCache:
     def __init__(self, n_layers: int, n_loops: int, n_heads_q: int, n_heads_kv: int,
                  head_dim: int, window: int, batch: int, capacity: int, max_block: int,
                  anchor: int = _r.RIPE_ANCHOR_QUERY, device="cuda", stream=None,
-                 tuning: Optional[dict] = None):
+                 tuning: Optional[dict] = None, image: Optional[torch.Tensor] = None):
+        """image: a copy of another cache's storage (same configuration) to
+        resume from, e.g. a checkpoint on the host; None starts empty."""
         self.cfg = _r.config(n_layers, n_loops, n_heads_q, n_heads_kv, head_dim, window, batch,
                              capacity, max_block, anchor)
         nbytes = _r.ripe_cache_bytes(self.cfg)
@@ -35,7 +37,15 @@ class RipeCache:
         self.storage = torch.empty(nbytes, dtype=torch.uint8, device=device)
         if self.storage.data_ptr() % 256:
             raise RuntimeError("storage allocation is not 256-byte aligned")
-        self.handle = _r.ripe_cache_create(self.cfg, self.storage, stream)
+        if image is None:
+            self.handle = _r.ripe_cache_create(self.cfg, self.storage, stream)
+        else:
+            if image.dtype != torch.uint8 or image.numel() != nbytes:
+                raise ValueError("image must be %d bytes of uint8" % nbytes)
+            self.storage.copy_(image.reshape(-1))
+            if stream is not None:          # the copy ran on the current stream
+                torch.cuda.current_stream(self.storage.device).synchronize()
+            self.handle = _r.ripe_cache_open(self.cfg, self.storage, stream)
         self._ws = None
         tuning = DEFAULT_TUNING if tuning is None else tuning
         if tuning:

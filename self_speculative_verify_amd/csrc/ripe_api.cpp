@@ -14,6 +14,7 @@
 #include <mutex>
 #include <new>
 #include <unordered_set>
+#include <utility>
 #include <vector>
 
 using ripe::Geometry;
@@ -142,6 +143,29 @@ int32_t ripe_max_batch(const ripe_config* cfg, size_t budget_bytes) {
     return lo;
 }
 
+namespace {
+
+// a registered handle over d_storage with the given committed lengths
+ripe_status new_handle(const Geometry& g, void* d_storage, std::vector<int32_t>&& lens, ripe_cache** out) {
+    ripe_cache* c = new (std::nothrow) ripe_cache;
+    if (!c) return RIPE_EDEVICE;
+    c->g = g;
+    c->storage = static_cast<uint8_t*>(d_storage);
+    c->lens = std::move(lens);
+    std::memset(&c->tuning, 0, sizeof(c->tuning));
+    c->device = -1;
+    c->rows_buf.assign(ripe::kMaxRowsPerCall, 0u);
+    c->plans_buf.resize((ripe::kMaxRowsPerCall + ripe::kMaxRowsPerLaunch - 1) / ripe::kMaxRowsPerLaunch);
+    {
+        std::lock_guard<std::mutex> lock(g_handles_mu);
+        handles().insert(c);
+    }
+    *out = c;
+    return RIPE_OK;
+}
+
+}  // namespace
+
 ripe_status ripe_cache_create(const ripe_config* cfg, void* d_storage, size_t bytes,
                               hipStream_t stream, ripe_cache** out) {
     if (!out) return RIPE_EINVAL;
@@ -149,25 +173,25 @@ ripe_status ripe_cache_create(const ripe_config* cfg, void* d_storage, size_t by
     if (!valid_config(cfg) || !d_storage || !aligned(d_storage, 256)) return RIPE_EINVAL;
     const Geometry g = geometry(cfg);
     if (bytes < (size_t)g.total) return RIPE_EINVAL;
-    ripe_cache* c = new (std::nothrow) ripe_cache;
-    if (!c) return RIPE_EDEVICE;
-    c->g = g;
-    c->storage = static_cast<uint8_t*>(d_storage);
-    c->lens.assign((size_t)g.n_layers * g.B, 0);
-    std::memset(&c->tuning, 0, sizeof(c->tuning));
-    c->device = -1;
-    c->rows_buf.assign(ripe::kMaxRowsPerCall, 0u);
-    c->plans_buf.resize((ripe::kMaxRowsPerCall + ripe::kMaxRowsPerLaunch - 1) / ripe::kMaxRowsPerLaunch);
-    if (hipMemsetAsync(d_storage, 0, (size_t)g.total, stream) != hipSuccess) {
-        delete c;
+    if (hipMemsetAsync(d_storage, 0, (size_t)g.total, stream) != hipSuccess) return RIPE_EDEVICE;
+    return new_handle(g, d_storage, std::vector<int32_t>((size_t)g.n_layers * g.B, 0), out);
+}
+
+ripe_status ripe_cache_open(const ripe_config* cfg, void* d_storage, size_t bytes,
+                            hipStream_t stream, ripe_cache** out) {
+    if (!out) return RIPE_EINVAL;
+    *out = nullptr;
+    if (!valid_config(cfg) || !d_storage || !aligned(d_storage, 256)) return RIPE_EINVAL;
+    const Geometry g = geometry(cfg);
+    if (bytes < (size_t)g.total) return RIPE_EINVAL;
+    std::vector<int32_t> lens((size_t)g.n_layers * g.B, 0);
+    if (hipMemcpyAsync(lens.data(), static_cast<const uint8_t*>(d_storage) + g.off_lens,
+                       lens.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
         return RIPE_EDEVICE;
-    }
-    {
-        std::lock_guard<std::mutex> lock(g_handles_mu);
-        handles().insert(c);
-    }
-    *out = c;
-    return RIPE_OK;
+    for (const int32_t L : lens)
+        if (L < 0 || (int64_t)L > g.cap) return RIPE_EINVAL;
+    return new_handle(g, d_storage, std::move(lens), out);
 }
 
 void ripe_destroy(ripe_cache* cache) {

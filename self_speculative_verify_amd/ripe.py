@@ -19,7 +19,8 @@ __all__ = [
     "RIPE_SECTION_LENS", "RIPE_SECTION_DEEP_K", "RIPE_SECTION_DEEP_V",
     "RIPE_SECTION_RING_K", "RIPE_SECTION_RING_V", "RIPE_SECTION_END",
     "RipeConfig", "RipeKVView", "RipeError", "library_path", "load",
-    "ripe_cache_bytes", "ripe_section_offset", "ripe_max_batch", "ripe_cache_create", "ripe_destroy",
+    "ripe_cache_bytes", "ripe_section_offset", "ripe_max_batch", "ripe_cache_create",
+    "ripe_cache_open", "ripe_destroy",
     "ripe_get_lengths", "ripe_append", "ripe_workspace_bytes", "ripe_verify_attn",
     "ripe_draft_attn", "RipeTuning", "ripe_set_tuning",
     "ripe_status_string", "kv_view", "null_view", "config",
@@ -81,6 +82,8 @@ def load():
         L.ripe_max_batch.argtypes = [CFG, SZ]
         L.ripe_cache_create.restype = I32
         L.ripe_cache_create.argtypes = [CFG, P, SZ, P, ctypes.POINTER(P)]
+        L.ripe_cache_open.restype = I32
+        L.ripe_cache_open.argtypes = [CFG, P, SZ, P, ctypes.POINTER(P)]
         L.ripe_destroy.restype = None
         L.ripe_destroy.argtypes = [P]
         L.ripe_get_lengths.restype = I32
@@ -171,6 +174,17 @@ def ripe_cache_create(cfg: RipeConfig, storage: torch.Tensor, stream=None) -> ct
     _check(load().ripe_cache_create(ctypes.byref(cfg), ctypes.c_void_p(storage.data_ptr()),
                                     storage.numel(), _stream(stream), ctypes.byref(h)),
            "ripe_cache_create")
+    return h
+
+
+def ripe_cache_open(cfg: RipeConfig, storage: torch.Tensor, stream=None) -> ctypes.c_void_p:
+    """Bind a handle to a uint8 device tensor that already holds a cache image."""
+    if not storage.is_cuda or storage.dtype != torch.uint8 or not storage.is_contiguous():
+        raise ValueError("storage must be a contiguous uint8 device tensor")
+    h = ctypes.c_void_p()
+    _check(load().ripe_cache_open(ctypes.byref(cfg), ctypes.c_void_p(storage.data_ptr()),
+                                  storage.numel(), _stream(stream), ctypes.byref(h)),
+           "ripe_cache_open")
     return h
 
 

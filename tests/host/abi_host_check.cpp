@@ -7,7 +7,8 @@
 //
 // Checks: validation paths leave no side effect (nothing launched, lengths
 // unchanged); a destroyed handle is refused, and destroying it again is
-// harmless; the workspace that ripe_workspace_bytes returns covers the
+// harmless; re-opening storage takes its lengths from the image and refuses
+// a length outside [0, capacity]; the workspace that ripe_workspace_bytes returns covers the
 // partial states every launch of a call writes, over a sweep of shapes, row
 // counts (one launch, several launches with a short last one) and forced
 // launch choices.  Exit status 0 and a last line "host checks passed" on
@@ -50,6 +51,17 @@ extern "C" hipError_t hipMemsetAsync(void* p, int v, size_t n, hipStream_t) {
     if (p == rec.real) std::memset(p, v, n < rec.real_bytes ? n : rec.real_bytes);
     return hipSuccess;
 }
+
+extern "C" hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMemcpyKind, hipStream_t) {
+    // only the lengths section exists in host memory
+    const uint8_t* s = static_cast<const uint8_t*>(src);
+    const uint8_t* r = static_cast<const uint8_t*>(rec.real);
+    if (s < r || s + n > r + rec.real_bytes) return hipErrorInvalidValue;
+    std::memcpy(dst, src, n);
+    return hipSuccess;
+}
+
+extern "C" hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 
 extern "C" hipError_t hipPointerGetAttributes(hipPointerAttribute_t* a, const void*) {
     std::memset(a, 0, sizeof(*a));
@@ -381,8 +393,43 @@ static void check_balance_split() {
     (void)rng;
 }
 
+static void check_open() {
+    Fake f;
+    CHECK(make(f, config(2, 4, 4, 2, 64, 8, 3, 100, 4)), "create");
+    CHECK(append_all(f, {100, 7, 0}) == RIPE_OK, "append");
+    const size_t bytes = ripe_cache_bytes(&f.cfg);
+    uint8_t* base = static_cast<uint8_t*>(const_cast<void*>(rec.real));
+    const int appends = rec.appends;
+    // a second handle over the same image: the lengths come from storage
+    ripe_cache* h2 = nullptr;
+    CHECK(ripe_cache_open(&f.cfg, base, bytes, nullptr, &h2) == RIPE_OK && h2, "open");
+    int32_t lens[3] = {-1, -1, -1};
+    CHECK(h2 && ripe_get_lengths(h2, 0, lens) == RIPE_OK && lens[0] == 100 && lens[1] == 7 && lens[2] == 0,
+          "lengths of the opened image");
+    CHECK(h2 && ripe_get_lengths(h2, 1, lens) == RIPE_OK && lens[0] == 0 && lens[2] == 0, "layer 1");
+    CHECK(h2 && ripe_append(h2, 0, std::vector<int32_t>{1, 0, 0}.data(), view(), view(), view(), view(),
+                            nullptr) == RIPE_ECAPACITY, "capacity from the image");
+    ripe_destroy(h2);
+    // a stored length out of range, a short or misaligned storage: refused, no handle
+    int32_t* dev_lens = reinterpret_cast<int32_t*>(base);
+    for (const int32_t badlen : {101, -1}) {
+        const int32_t keep = dev_lens[4];
+        dev_lens[4] = badlen;                     // layer 1, sequence 1
+        ripe_cache* h3 = reinterpret_cast<ripe_cache*>(&rec);
+        CHECK(ripe_cache_open(&f.cfg, base, bytes, nullptr, &h3) == RIPE_EINVAL && !h3, "length %d", badlen);
+        dev_lens[4] = keep;
+    }
+    ripe_cache* h4 = nullptr;
+    CHECK(ripe_cache_open(&f.cfg, base, bytes - 1, nullptr, &h4) == RIPE_EINVAL && !h4, "short storage");
+    CHECK(ripe_cache_open(&f.cfg, base + 4, bytes, nullptr, &h4) == RIPE_EINVAL && !h4, "misaligned");
+    CHECK(ripe_cache_open(&f.cfg, base, bytes, nullptr, nullptr) == RIPE_EINVAL, "null out");
+    CHECK(rec.appends == appends, "open launched work");
+    ripe_destroy(f.h);
+}
+
 int main() {
     check_validation();
+    check_open();
     check_balance_split();
     check_workspace_sweep();
     if (rec.failures) {
