@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--tuning", default=None, metavar="JSON",
                     help="fixed launch choices for every cache (fields of ripe_tuning), e.g. "
-                         "'{\"rows_waves\": 4}'")
+                         "'{\"keys_waves\": 8}'")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the comparison rounds (Huginn-scale windows, GQA deepest-only "
                          "and full cache, the small shape in both layouts)")
