@@ -539,13 +539,16 @@ def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=No
     for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    # an event after every step: the mean over the K steps and the spread of
+    # single steps come from the same timed region
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record()
     for k in range(steps):
         step(k)
-    stop.record()
+        marks[k + 1].record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / max(steps, 1)
+    ms = marks[0].elapsed_time(marks[steps]) / max(steps, 1)
+    step_ms = [marks[k].elapsed_time(marks[k + 1]) for k in range(steps)]
     del graphs
 
     if n_rep is None:
@@ -562,7 +565,16 @@ def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=No
             evs[j + 1].record()
         torch.cuda.synchronize()
         launch_ms += [evs[j].elapsed_time(evs[j + 1]) for j in range(n_ev)]
-    return ms, launch_ms
+    return ms, launch_ms, step_ms
+
+
+def spread(xs, digits=5):
+    """Median, 10th and 90th percentile of a list of times."""
+    v = sorted(xs)
+    if not v:
+        return None
+    q = lambda f: v[min(len(v) - 1, max(0, int(round(f * (len(v) - 1)))))]
+    return {"median": round(q(0.5), digits), "p10": round(q(0.1), digits), "p90": round(q(0.9), digits)}
 
 
 def roofline_of(u_call, f_call, launch_s):
@@ -608,7 +620,7 @@ def comparisons(dev, steps, warmup):
         copies = copies_for(u_call * wl.n_layers)
         print(f"bench: comparison {name} W={w} copies={copies}", file=sys.stderr, flush=True)
         setups = build_setups(wl, window, wl.anchor, calls, copies, dev)
-        ms, launch_ms = time_setups(setups, wl, calls, steps, warmup, n_rep=max(4, min(steps, 10)))
+        ms, launch_ms, _ = time_setups(setups, wl, calls, steps, warmup, n_rep=max(4, min(steps, 10)))
         del setups
         torch.cuda.empty_cache()
         launch_s = sum(launch_ms) / len(launch_ms) / 1e3
@@ -703,7 +715,7 @@ def main():
 
     setups = build_setups(wl, window, anchor, calls, copies, dev)
     print("bench: caches built", file=sys.stderr, flush=True)
-    ms, launch_ms = time_setups(setups, wl, calls, args.steps, args.warmup, args.eager, sw)
+    ms, launch_ms, step_ms = time_setups(setups, wl, calls, args.steps, args.warmup, args.eager, sw)
     t = ms / 1e3
     launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     u_call, f_call = u_layer / len(calls), f_layer / len(calls)
@@ -732,6 +744,7 @@ def main():
     roof = roofline_of(u_call, f_call, launch_s)
     roof["traffic"] = traffic
     roof["launch_us"] = round(launch_s * 1e6, 3)
+    roof["launch_us_spread"] = spread([x * 1e3 for x in launch_ms], 3)
     roof["algorithmic_bytes"] = round(u_call)
     roof["algorithmic_flops"] = round(f_call)
 
@@ -753,6 +766,7 @@ def main():
     res = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "step_ms_spread": spread(step_ms),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": wl.n_layers, "loops": wl.n_loops,
