@@ -46,6 +46,7 @@ MALL_BYTES = 256 << 20
 CPU_SAMPLE_S = 10.0             # oracle layers are timed until this much CPU time is spent
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_traffic_counters.txt")
 SPIN_CYCLES = 20_000_000        # a spinning kernel that covers the host's enqueue of timed launches
+SPIN_CYCLES_PER_CALL = 150_000  # ... of one call (~60 us of host work)
 
 
 def parse():
@@ -495,8 +496,9 @@ def build_setups(wl, window, anchor, calls, copies, dev):
 
 def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=None):
     """Step time (ms; each copy's round replayed from a HIP graph, rotating
-    over the copies) and the durations of single calls (ms), timed with
-    events queued behind a spinning kernel so no host gap falls between them."""
+    over the copies), the time of each timed step, and the durations of
+    single calls (ms), timed with events in one back-to-back sequence queued
+    behind a spinning kernel so no host gap falls between them."""
     import torch
     copies = len(setups)
 
@@ -553,18 +555,24 @@ def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=No
 
     if n_rep is None:
         n_rep = max(1, min(steps, 20 if len(calls) == 1 else 2))
-    launch_ms = []
+    # n_rep rounds back to back in one sequence, as the timed steps run them,
+    # behind one spinning kernel that outlasts the host's enqueue of them all
+    # (calls that follow an idle gap run while the clock is still settling)
     n_ev = len(calls) * wl.n_layers
+    total = n_rep * n_ev
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(total + 1)]
+    torch.cuda._sleep(max(SPIN_CYCLES, SPIN_CYCLES_PER_CALL * total))
+    evs[0].record()
     for k in range(n_rep):
-        torch.cuda._sleep(SPIN_CYCLES)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)]
         s = setups[k % copies]
-        evs[0].record()
         for j in range(n_ev):
             run_call(s, j // wl.n_layers, j % wl.n_layers)
-            evs[j + 1].record()
-        torch.cuda.synchronize()
-        launch_ms += [evs[j].elapsed_time(evs[j + 1]) for j in range(n_ev)]
+            evs[k * n_ev + j + 1].record()
+    if torch.cuda.current_stream().query():
+        print("bench: the spin ended before the calls were enqueued; call times include host gaps",
+              file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    launch_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(total)]
     return ms, launch_ms, step_ms
 
 
