@@ -556,12 +556,15 @@ def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=No
     if n_rep is None:
         n_rep = max(1, min(steps, 20 if len(calls) == 1 else 2))
     # n_rep rounds back to back in one sequence, as the timed steps run them,
-    # behind one spinning kernel that outlasts the host's enqueue of them all
+    # behind one spinning kernel that outlasts the host's enqueue of them all,
+    # and after one untimed round, as the timed steps follow the warm-up ones
     # (calls that follow an idle gap run while the clock is still settling)
     n_ev = len(calls) * wl.n_layers
     total = n_rep * n_ev
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(total + 1)]
-    torch.cuda._sleep(max(SPIN_CYCLES, SPIN_CYCLES_PER_CALL * total))
+    torch.cuda._sleep(max(SPIN_CYCLES, SPIN_CYCLES_PER_CALL * (total + n_ev)))
+    for j in range(n_ev):
+        run_call(setups[-1], j // wl.n_layers, j % wl.n_layers)
     evs[0].record()
     for k in range(n_rep):
         s = setups[k % copies]
