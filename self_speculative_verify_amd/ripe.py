@@ -6,6 +6,7 @@ binding raises if the library has not been built; there is no fallback.
 """
 from __future__ import annotations
 
+import array
 import ctypes
 import os
 from typing import Optional, Sequence
@@ -127,8 +128,11 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def _i32_array(xs: Sequence[int]):
-    arr = (ctypes.c_int32 * len(xs))(*[int(x) for x in xs])
-    return arr
+    """Host int32 array of xs (ints, or objects with __index__) for a pointer
+    argument; built in C through array.array, which is several times faster
+    than element-wise ctypes construction for the 256-row calls."""
+    a = array.array("i", xs)
+    return (ctypes.c_int32 * len(a)).from_buffer(a)
 
 
 def config(n_layers, n_loops, n_heads_q, n_heads_kv, head_dim, window, batch, capacity,
