@@ -538,19 +538,27 @@ def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=No
         else:
             graphs[k % copies].replay()
 
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record()
     for k in range(warmup):
         step(k)
+    w1.record()
     torch.cuda.synchronize()
-    # an event after every step: the mean over the K steps and the spread of
-    # single steps come from the same timed region
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # an event after every step, so the mean over the K steps and the spread
+    # of single steps come from the same timed region; only where a step is
+    # long enough that recording the events cannot make the host the bottleneck
+    per_step = warmup > 0 and w0.elapsed_time(w1) / warmup >= 0.5
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step else 2)]
     marks[0].record()
     for k in range(steps):
         step(k)
-        marks[k + 1].record()
+        if per_step:
+            marks[k + 1].record()
+    if not per_step:
+        marks[-1].record()
     torch.cuda.synchronize()
-    ms = marks[0].elapsed_time(marks[steps]) / max(steps, 1)
-    step_ms = [marks[k].elapsed_time(marks[k + 1]) for k in range(steps)]
+    ms = marks[0].elapsed_time(marks[-1]) / max(steps, 1)
+    step_ms = [marks[k].elapsed_time(marks[k + 1]) for k in range(steps)] if per_step else []
     del graphs
 
     if n_rep is None:
