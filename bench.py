@@ -47,6 +47,7 @@ CPU_SAMPLE_S = 10.0             # oracle layers are timed until this much CPU ti
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_traffic_counters.txt")
 SPIN_CYCLES = 20_000_000        # a spinning kernel that covers the host's enqueue of timed launches
 SPIN_CYCLES_PER_CALL = 300_000  # ... of one call (~60 us of host work, more under a profiler)
+MAX_SEQUENCE_CALLS = 160        # calls timed back to back behind one spin
 
 
 def parse():
@@ -567,11 +568,16 @@ def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=No
     # behind one spinning kernel that outlasts the host's enqueue of them all,
     # and after one untimed round, as the timed steps follow the warm-up ones
     # (calls that follow an idle gap run while the clock is still settling)
+    # (each call queues two kernels and an event: the sequence stays well
+    # inside the hardware queue, which would otherwise block the host until
+    # the spin ends and leave gaps between the calls)
     n_ev = len(calls) * wl.n_layers
+    n_rep = max(1, min(n_rep, MAX_SEQUENCE_CALLS // n_ev))
+    n_warm = min(n_ev, 32)
     total = n_rep * n_ev
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(total + 1)]
-    torch.cuda._sleep(max(SPIN_CYCLES, SPIN_CYCLES_PER_CALL * (total + n_ev)))
-    for j in range(n_ev):
+    torch.cuda._sleep(max(SPIN_CYCLES, SPIN_CYCLES_PER_CALL * (total + n_warm)))
+    for j in range(n_warm):
         run_call(setups[-1], j // wl.n_layers, j % wl.n_layers)
     evs[0].record()
     for k in range(n_rep):
