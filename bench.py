@@ -48,6 +48,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_traffic_counters.txt")
 SPIN_CYCLES = 20_000_000        # a spinning kernel that covers the host's enqueue of timed launches
 SPIN_CYCLES_PER_CALL = 300_000  # ... of one call (~60 us of host work, more under a profiler)
 MAX_SEQUENCE_CALLS = 160        # calls timed back to back behind one spin
+MAX_WARM_CALLS = 64             # untimed calls before them ...
+WARM_MS = 25.0                  # ... worth this much GPU time where they are long
 
 
 def parse():
@@ -565,20 +567,23 @@ def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=No
     if n_rep is None:
         n_rep = max(1, min(steps, 20 if len(calls) == 1 else 2))
     # n_rep rounds back to back in one sequence, as the timed steps run them,
-    # behind one spinning kernel that outlasts the host's enqueue of them all,
-    # and after one untimed round, as the timed steps follow the warm-up ones
-    # (calls that follow an idle gap run while the clock is still settling)
-    # (each call queues two kernels and an event: the sequence stays well
-    # inside the hardware queue, which would otherwise block the host until
-    # the spin ends and leave gaps between the calls)
+    # after untimed calls worth WARM_MS of GPU time: the clock drops while the
+    # GPU idles and takes ~20 ms of work to recover (a ragged call runs 720 us
+    # right after an idle gap and 535 us once the clock has settled).  Calls
+    # shorter than the host's enqueue of one (~0.2 ms) queue behind a spinning
+    # kernel instead, so that no host gap falls between them.  Each call queues
+    # two kernels and an event: the sequence stays well inside the hardware
+    # queue, which would otherwise block the host and leave gaps.
     n_ev = len(calls) * wl.n_layers
     n_rep = max(1, min(n_rep, MAX_SEQUENCE_CALLS // n_ev))
-    n_warm = min(n_ev, 32)
+    per_call = ms / n_ev
+    n_warm = max(1, min(MAX_WARM_CALLS, math.ceil(WARM_MS / max(per_call, 1e-3))))
     total = n_rep * n_ev
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(total + 1)]
-    torch.cuda._sleep(max(SPIN_CYCLES, SPIN_CYCLES_PER_CALL * (total + n_warm)))
+    if per_call < 0.2:
+        torch.cuda._sleep(max(SPIN_CYCLES, SPIN_CYCLES_PER_CALL * (total + n_warm)))
     for j in range(n_warm):
-        run_call(setups[-1], j // wl.n_layers, j % wl.n_layers)
+        run_call(setups[-1], (j % n_ev) // wl.n_layers, j % wl.n_layers)
     evs[0].record()
     for k in range(n_rep):
         s = setups[k % copies]
@@ -586,8 +591,8 @@ def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=No
             run_call(s, j // wl.n_layers, j % wl.n_layers)
             evs[k * n_ev + j + 1].record()
     if torch.cuda.current_stream().query():
-        print("bench: the spin ended before the calls were enqueued; call times include host gaps",
-              file=sys.stderr, flush=True)
+        print("bench: the GPU ran out of queued work before the calls were enqueued; call times "
+              "include host gaps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     launch_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(total)]
     return ms, launch_ms, step_ms
