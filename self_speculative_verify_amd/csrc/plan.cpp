@@ -61,8 +61,18 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
                bool draft, const Tuning& t) {
     Plan p;
     p.M = rows_here * (g.Hq / g.Hkv);
-    // the rows kernel pays off once a KV head carries a hundred row-heads or more
-    p.rows_kernel = draft ? false : t.kernel ? t.kernel == 2 : p.M >= 128;
+    int64_t lmax = 0;
+    for (int b = 0; b < g.B; ++b) lmax = std::max<int64_t>(lmax, lens[b]);
+    // The rows kernel pays off once a KV head carries a hundred row-heads or
+    // more, unless most committed positions lie in the window at a head size
+    // without private waves: each loop's ring tiles, which only that loop's
+    // rows read, then stream past the other row groups of a rows workgroup,
+    // while every wave of a keys workgroup works on its one row block (GQA
+    // shape, L = 4096: 400 against 560 us at W = 4000, 366 against 448 at
+    // W = 3072, equal at W = 2048, the rows kernel ahead at W = 1024).
+    const bool ring_heavy = g.R > 1 && lmax > 0 && !rows_private_waves(g.d, rows_max_row_tiles(g.d)) &&
+                            5 * std::min<int64_t>(g.WR, lmax) >= 3 * lmax;
+    p.rows_kernel = draft ? false : t.kernel ? t.kernel == 2 : p.M >= 128 && !ring_heavy;
     const int64_t heads = (int64_t)g.B * g.Hkv;
     int rows_per_item;
     if (p.rows_kernel) {
@@ -80,8 +90,6 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
     p.priv = p.rows_kernel && rows_private_waves(g.d, p.rt) &&
              (t.private_waves ? t.private_waves == 2 : (g.R > 1 && g.WR > 0));
     p.nrb = (p.M + rows_per_item - 1) / rows_per_item;
-    int64_t lmax = 0;
-    for (int b = 0; b < g.B; ++b) lmax = std::max<int64_t>(lmax, lens[b]);
     // workgroups of one (sequence, chunk) pair, and of the whole call unsplit
     const int64_t units = (int64_t)g.Hkv * p.nrb;
     const int64_t base = g.B * units;
