@@ -106,32 +106,47 @@ Plan make_plan(const Geometry& g, const int32_t* lens, int rows_here, const uint
     // workgroup target: one round of the rows kernel; for the keys kernel
     // (two workgroups per CU) a second round only pays off on long contexts,
     // where the chunks stay long enough to outweigh the extra partial states
-    const int64_t slots = draft || auto_wide ? 0 : t.items_target ? t.items_target
-                                    : (p.rows_kernel || lmax <= 4096 ? 256 : 512);
+    const int64_t slots_max = draft || auto_wide ? 0 : t.items_target ? t.items_target
+                                        : (p.rows_kernel || lmax <= 4096 ? 256 : 512);
     const int64_t min_chunk = t.min_chunk ? up(t.min_chunk, 32)
                                           : std::max<int64_t>(256, 8 * rows_per_item);
     // One chunk length for every sequence, from their total: the pairs that
     // fit one round of slots share the work evenly however ragged the
     // lengths are (a sequence gets ceil((L + cx) / cl) chunks).
+    int64_t sum = 0;
+    for (int b = 0; b < g.B; ++b) sum += lens[b] > 0 ? lens[b] + cx : 0;
+    auto chunk_len = [&](int64_t slots) {
+        const int64_t pairs = std::max<int64_t>(1, slots / units);
+        return std::max<int64_t>(min_chunk, up((sum + pairs - 1) / pairs, 32));
+    };
+    int64_t slots = slots_max;
+    if (slots == 512 && !t.items_target && base < 256) {
+        // ... unless one workgroup per CU already holds the call: a split for
+        // 256 slots that stays within 256 workgroups beats the two-per-CU one
+        // (the wave, 55 heads at L = 8192: 4 chunks, 220 workgroups, 45.7 us
+        // against 9 chunks, 495 workgroups, 48.1 us; 5 chunks, 275
+        // workgroups: 56.7 us).  Where the ceilings of a ragged batch push
+        // that split past 256 workgroups, two per CU stay (a ragged draft
+        // pass: 87.6 against 96.2 us per call).
+        const int64_t cl1 = chunk_len(256);
+        int64_t n = 0;
+        for (int b = 0; b < g.B; ++b) n += lens[b] > 0 ? (lens[b] + cx + cl1 - 1) / cl1 : 1;
+        if (units * n <= 256) slots = 256;
+    }
     int64_t cl = 0, nc_cap = 1;
     if (base < slots) {
-        int64_t sum = 0;
-        for (int b = 0; b < g.B; ++b) sum += lens[b] > 0 ? lens[b] + cx : 0;
-        const int64_t pairs = slots / units;
-        cl = std::max<int64_t>(min_chunk, up((sum + pairs - 1) / std::max<int64_t>(pairs, 1), 32));
+        cl = chunk_len(slots);
         // a bound on the chunk count that never falls as rows or lengths grow
-        nc_cap = std::max<int64_t>(1, std::min<int64_t>(pairs, (lmax + cx + min_chunk - 1) / min_chunk));
+        // (taken at the larger target, which the choice above can only lower)
+        nc_cap = std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(1, slots_max / units),
+                                                        (lmax + cx + min_chunk - 1) / min_chunk));
     } else if (p.rows_kernel && !draft && !t.items_target) {
         // One round of row blocks fills the chip, but a sequence much longer
         // than the mean load of a workgroup slot would still finish last (a
         // ragged batch): split the sequences into chunks no longer than that
         // mean, and the launch hands out the longest items first.
-        int64_t sum = 0, sum_l = 0;
-        for (int b = 0; b < g.B; ++b)
-            if (lens[b] > 0) {
-                sum += lens[b] + cx;
-                sum_l += lens[b];
-            }
+        int64_t sum_l = 0;
+        for (int b = 0; b < g.B; ++b) sum_l += lens[b] > 0 ? lens[b] : 0;
         const int64_t mean = (units * sum + slots - 1) / slots;
         if (lmax + cx > mean + mean / 8) cl = std::max<int64_t>(min_chunk, up(mean, 32));
         // for any row set of this size (cx at most this one): chunks are never
