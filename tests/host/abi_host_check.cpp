@@ -320,6 +320,8 @@ static void check_workspace_sweep() {
         {32, 55, 55, 96, 1024, 1, 8, {1024}},
         {8, 2, 2, 64, 16, 1, 4, {128}},
         {32, 32, 8, 128, FULL, 4, 8, {4096, 100, 0, 4000}},
+        {32, 32, 8, 128, 3072, 4, 8, {4096, 4096, 3000, 4096}},   // window over 60%: keys kernel
+        {32, 55, 55, 96, 64, 1, 8, {8192}},                        // one keys workgroup per CU
         {4, 4, 2, 64, 8, 70, 3, {}},
         {32, 55, 55, 96, 64, 1, 32, {8192}},
         {1, 8, 2, 128, 0, 3, 40, {3000, 1, 600}},
