@@ -4,6 +4,7 @@ from __future__ import annotations
 from typing import List, Sequence
 
 import numpy as np
+import torch
 
 from synth import Workload
 
@@ -76,3 +77,29 @@ def use_tuning(monkeypatch, name: str) -> None:
     """Make every RipeCache created from now on use the named launch choices."""
     from self_speculative_verify_amd import cache as cache_mod
     monkeypatch.setattr(cache_mod, "DEFAULT_TUNING", TUNINGS[name])
+
+
+# Guard bands: a buffer handed to the library as the middle of a larger
+# allocation whose edges hold a fixed byte pattern.
+GUARD = 4096          # bytes on each side (keeps the middle 256-byte aligned)
+PATTERN = 0xA5        # every guard byte; a float of four such bytes is -2.9e-16
+
+
+def guarded(nbytes: int, device="cuda"):
+    """(whole allocation, middle nbytes) with the pattern everywhere."""
+    full = torch.full((2 * GUARD + nbytes,), PATTERN, dtype=torch.uint8, device=device)
+    return full, full[GUARD:GUARD + nbytes]
+
+
+def edges_intact(full: torch.Tensor, nbytes: int) -> bool:
+    head = full[:GUARD]
+    tail = full[GUARD + nbytes:]
+    return (tail.numel() == GUARD and bool(torch.all(head == PATTERN).item())
+            and bool(torch.all(tail == PATTERN).item()))
+
+
+def all_written(middle: torch.Tensor) -> bool:
+    """No 4-byte word of the middle still holds the pattern."""
+    words = middle.view(torch.int32)
+    pat = int(np.array([PATTERN] * 4, np.uint8).view(np.int32)[0])
+    return not bool(torch.any(words == pat).item())
