@@ -497,14 +497,9 @@ def build_setups(wl, window, anchor, calls, copies, dev):
     return setups
 
 
-def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=None):
-    """Step time (ms; each copy's round replayed from a HIP graph, rotating
-    over the copies), the time of each timed step, and the durations of
-    single calls (ms), timed with events in one back-to-back sequence queued
-    behind a spinning kernel so no host gap falls between them."""
-    import torch
-    copies = len(setups)
-
+def round_runner(wl, calls, sw=None):
+    """(run_call, run_round): one call of one layer on a cache copy, and a
+    whole step's calls in the order a forward pass runs them."""
     def run_call(setup, k, layer):
         cache, ins, outs = setup
         qs, bk, bv = ins[layer]
@@ -522,6 +517,37 @@ def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=No
         for k in range(len(calls)):
             for layer in range(wl.n_layers):
                 run_call(setup, k, layer)
+
+    return run_call, run_round
+
+
+def eager_step_ms(setups, wl, calls, steps, sw=None):
+    """Mean step time (ms) with every call of the step issued from Python
+    through the binding, no graph: the host work of the calls included.
+    Rotates over the cache copies like the graph replays; a few untimed
+    steps first."""
+    import torch
+    _, run_round = round_runner(wl, calls, sw)
+    copies = len(setups)
+    for k in range(min(steps, 3)):
+        run_round(setups[k % copies])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(steps):
+        run_round(setups[k % copies])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / max(steps, 1)
+
+
+def time_setups(setups, wl, calls, steps, warmup, eager=False, sw=None, n_rep=None):
+    """Step time (ms; each copy's round replayed from a HIP graph, rotating
+    over the copies), the time of each timed step, and the durations of
+    single calls (ms), timed with events in one back-to-back sequence queued
+    behind a spinning kernel so no host gap falls between them."""
+    import torch
+    copies = len(setups)
+    run_call, run_round = round_runner(wl, calls, sw)
 
     for s in setups:            # eager warm-up (allocates workspaces outside capture)
         run_round(s)
@@ -746,6 +772,8 @@ def main():
     setups = build_setups(wl, window, anchor, calls, copies, dev)
     print("bench: caches built", file=sys.stderr, flush=True)
     ms, launch_ms, step_ms = time_setups(setups, wl, calls, args.steps, args.warmup, args.eager, sw)
+    # the same steps issued eagerly (host work included), next to the graphs
+    ms_eager = None if args.eager else eager_step_ms(setups, wl, calls, args.steps, sw)
     t = ms / 1e3
     launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     u_call, f_call = u_layer / len(calls), f_layer / len(calls)
@@ -818,6 +846,10 @@ def main():
         "flops_per_step": f_layer * wl.n_layers,
         "kernel_sources": digest,
         "roofline": roof,
+        "host_inclusive": None if ms_eager is None else {
+            "ms_per_step": round(ms_eager, 5), "GB/s": round(u_round / ms_eager / 1e6, 2),
+            "tokens_per_s": round(n_tokens / ms_eager * 1e3, 1),
+            "timing": "the step's calls issued from Python through the binding, no graph"},
         "append": append,
         "comparisons": comp,
         "cpu_baseline": cpu,

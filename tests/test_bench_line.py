@@ -6,7 +6,8 @@ driver runs the default workload, and checks the line's keys and the
 relations between its numbers: value = unique bytes per step / step time,
 tokens/s = verified positions per step / step time, the roofline's fraction
 = achieved / peak and achieved = the algorithmic flops or bytes of a call /
-the call time, and a CPU baseline from the oracle.
+the call time, the host-inclusive (eager) step figures, and a CPU baseline
+from the oracle.
 """
 import json
 import os
@@ -55,3 +56,10 @@ def test_bench_line_of_the_small_shape():
     assert roof["achieved"] == pytest.approx(work / call_s, rel=2e-3)
     cpu = r["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1
+    # the same steps issued eagerly: host work included, never faster than
+    # the work itself by more than timing noise
+    hi = r["host_inclusive"]
+    te = hi["ms_per_step"] / 1e3
+    assert te > 0
+    assert hi["GB/s"] == pytest.approx(r["unique_kv_bytes_per_step"] / te / 1e9, rel=2e-3, abs=0.01)
+    assert hi["tokens_per_s"] == pytest.approx(4 / te, rel=2e-3)
