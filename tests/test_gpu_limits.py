@@ -1,6 +1,7 @@
 """GPU parity at the edges of the launch configuration: calls with more rows
 than one launch takes (256), batches larger than one append launch takes (64),
-draft blocks longer than one 32-key tile, and windows longer than the
+draft blocks longer than one 32-key tile up to the largest (256 positions),
+the most loops a configuration allows (255), and windows longer than the
 capacity.  Same bar as the other parity tests (bit-exact layout, max |dO| <=
 2e-3, relative LSE error <= 1e-5), against the fp64 oracle.
 """
@@ -72,6 +73,21 @@ def test_batch_larger_than_one_append_launch():
 @pytest.mark.parametrize("D", [33, 40])
 def test_draft_block_longer_than_a_tile(D):
     run(Workload(f"blk{D}", 93, 1, 3, 4, 4, 96, 48, D, [200, 7], 0.88, grid_rows(D, 3)))
+
+
+def test_largest_draft_block():
+    """max_block = 256, the largest the row words hold: block offsets 0..255
+    (eight 32-key block tiles per loop), 512 rows in two launches."""
+    run(Workload("blk256", 98, 1, 2, 2, 1, 64, 300, 256, [40, 300], 0.88, grid_rows(256, 2),
+                 heavy_frac=0.05))
+
+
+@pytest.mark.parametrize("D", [1, 2])
+def test_most_loops(D):
+    """R = 255 loops, the most the row words hold: with one block position a
+    rows workgroup's 128 rows are 128 different loops (both halves of its
+    loop list full), with two the call takes two launches."""
+    run(Workload(f"r255d{D}", 99, 1, 255, 1, 1, 64, 8, D, [50], 0.88, grid_rows(D, 255)))
 
 
 @pytest.mark.parametrize("W", [500, WINDOW_FULL])
