@@ -225,3 +225,64 @@ def test_block_independence_on_gpu():
     so[:, idx2], sl[:, idx2] = o2, l2
     assert float((so - full_o).abs().max()) < 1e-5
     assert float((sl - full_l).abs().max()) < 1e-5
+
+
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_peaked_softmax_large_values(d):
+    """Two deep-plane keys per KV head take nearly all of every row-head's
+    softmax weight (scores ~8 sqrt(d) above the others and ~0.4 apart) and
+    carry values of magnitude ~40 of opposite sign.  Their weights are not
+    bf16 numbers: P.V with P rounded to bf16 alone would miss O by far more
+    than the tolerance (checked below on the CPU, from the exact weights),
+    while the hi/lo split of P stays within it (its own rounding, ~2^-18 of
+    a weight, times value components up to ~150, leaves a few 1e-4).  Runs
+    through every launch choice of the fixtures (the rows kernel's fast phase
+    included)."""
+    from synth import bf16_to_f32
+    H = _h()
+    R, HQ, HKV, W, D, L = 4, 4, 2, 8, 4, 600
+    rows = grid_rows(D, R)
+    wl = Workload(f"peak{d}", 81, 1, R, HQ, HKV, d, W, D, [L], 0.88, rows)
+    rng = np.random.default_rng(81 + d)
+    K = 0.05 * rng.standard_normal((HKV, L, d))
+    V = rng.standard_normal((HKV, L, d))
+    u = rng.standard_normal((HKV, d))
+    pairs = [(100 + 7 * g, 350 + 11 * g) for g in range(HKV)]       # both below L - W
+    for g, (a, b) in enumerate(pairs):
+        K[g, a] = u[g]
+        K[g, b] = u[g] + 0.05 * rng.standard_normal(d)
+        V[g, a] = 40.0 * rng.standard_normal(d)
+        V[g, b] = -V[g, a] + rng.standard_normal(d)
+    kb, vb = f32_to_bf16(K.astype(np.float32)), f32_to_bf16(V.astype(np.float32))
+    dk, dv = kb[None], vb[None]                                     # [1][Hkv][L][d]
+    wk = np.repeat(kb[None, None, :, L - W:], R - 1, axis=1)        # [1][R-1][Hkv][W][d]
+    wv = np.repeat(vb[None, None, :, L - W:], R - 1, axis=1)
+    grp = [h * HKV // HQ for h in range(HQ)]
+    q = f32_to_bf16(np.broadcast_to((8.0 * u[grp])[None, None], (1, len(rows), HQ, d)).astype(np.float32))
+    bk = f32_to_bf16((0.05 * rng.standard_normal((1, R, HKV, D, d))).astype(np.float32))
+    bv = f32_to_bf16(rng.standard_normal((1, R, HKV, D, d)).astype(np.float32))
+
+    # the premise, from the exact weights of the dominant pair (row 0, head 0)
+    # against the reference the kernels take there (key a's score: the tile
+    # that holds it moves the reference, key b's score is within the margin)
+    qf = bf16_to_f32(q[0, 0, 0]).astype(np.float64)
+    a, b = pairs[0]
+    s = np.array([bf16_to_f32(kb[0, a]) @ qf, bf16_to_f32(kb[0, b]) @ qf]) / np.sqrt(d)
+    p = np.exp(s - s[0])
+    p_bf = bf16_to_f32(f32_to_bf16(p.astype(np.float32))).astype(np.float64)
+    va, vb_ = bf16_to_f32(vb[0, a]).astype(np.float64), bf16_to_f32(vb[0, b]).astype(np.float64)
+    exact = (p[0] * va + p[1] * vb_) / p.sum()
+    rounded = (p_bf[0] * va + p_bf[1] * vb_) / p.sum()
+    assert np.max(np.abs(rounded - exact)) > 10 * TOL_O, "the inputs do not stress the weights' precision"
+
+    cache = H.make_cache(wl)
+    cache.append(0, [L], H.to_dev(dk), H.to_dev(dv), H.to_dev(wk), H.to_dev(wv))
+    oc = oracle.OracleCache(oracle.config_of(wl))
+    assert oc.append(0, [L], dk, dv, wk, wv) == oracle.ORA_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.storage.cpu().numpy(), oc.image), "layout differs from the oracle"
+    out, lse = cache.verify(0, rows, H.to_dev(q), H.to_dev(bk), H.to_dev(bv), D)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oc.verify(0, rows, q, bk, bv, D)
+    assert float(np.max(np.abs(ref_o))) > 1.0                       # the pair dominates O
+    assert_close(out, lse, ref_o, ref_l, f"peaked d={d}")
