@@ -286,3 +286,46 @@ def test_peaked_softmax_large_values(d):
     ref_o, ref_l = oc.verify(0, rows, q, bk, bv, D)
     assert float(np.max(np.abs(ref_o))) > 1.0                       # the pair dominates O
     assert_close(out, lse, ref_o, ref_l, f"peaked d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_rising_scores_rescale_every_tile(d):
+    """Committed keys whose scores rise by ~10 (log2 units) from one 32-key
+    tile to the next: every tile passes the exponent reference by more than
+    its margin, so the rescale of l and O (otherwise about once per row-head)
+    runs on every tile of every launch choice.  Deepest plane only (W = 0);
+    the last few committed keys dominate the softmax."""
+    from synth import bf16_to_f32
+    H = _h()
+    R, HQ, HKV, W, D, L = 4, 4, 2, 0, 4, 500
+    rows = grid_rows(D, R)
+    wl = Workload(f"rise{d}", 82, 1, R, HQ, HKV, d, W, D, [L], 0.88, rows)
+    rng = np.random.default_rng(82 + d)
+    u = rng.standard_normal((HKV, d))
+    step = 10.0 / 32 / (np.log2(np.e) / np.sqrt(d)) / d             # score rise per position / |u|^2
+    t = step * np.arange(L)
+    K = t[None, :, None] * u[:, None, :] + 0.05 * rng.standard_normal((HKV, L, d))
+    V = rng.standard_normal((HKV, L, d))
+    kb, vb = f32_to_bf16(K.astype(np.float32)), f32_to_bf16(V.astype(np.float32))
+    dk, dv = kb[None], vb[None]
+    wk = np.zeros((1, R - 1, HKV, 1, d), np.uint16)                 # no ring (W = 0)
+    grp = [h * HKV // HQ for h in range(HQ)]
+    q = f32_to_bf16(np.broadcast_to(u[grp][None, None], (1, len(rows), HQ, d)).astype(np.float32))
+    bk = f32_to_bf16((0.05 * rng.standard_normal((1, R, HKV, D, d))).astype(np.float32))
+    bv = f32_to_bf16(rng.standard_normal((1, R, HKV, D, d)).astype(np.float32))
+    # the premise: consecutive tiles' maxima (log2 units) differ by more than 8
+    qf = bf16_to_f32(q[0, 0, 0]).astype(np.float64)
+    x = (bf16_to_f32(kb[0]).astype(np.float64) @ qf) * np.log2(np.e) / np.sqrt(d)
+    tile_max = x[: L // 32 * 32].reshape(-1, 32).max(axis=1)
+    assert np.all(np.diff(tile_max) > 8.0)
+
+    cache = H.make_cache(wl)
+    cache.append(0, [L], H.to_dev(dk), H.to_dev(dv), None, None)
+    oc = oracle.OracleCache(oracle.config_of(wl))
+    assert oc.append(0, [L], dk, dv, wk, wk) == oracle.ORA_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.storage.cpu().numpy(), oc.image), "layout differs from the oracle"
+    out, lse = cache.verify(0, rows, H.to_dev(q), H.to_dev(bk), H.to_dev(bv), D)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oc.verify(0, rows, q, bk, bv, D)
+    assert_close(out, lse, ref_o, ref_l, f"rising d={d}")
