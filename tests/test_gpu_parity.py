@@ -329,3 +329,15 @@ def test_rising_scores_rescale_every_tile(d):
     torch.cuda.synchronize()
     ref_o, ref_l = oc.verify(0, rows, q, bk, bv, D)
     assert_close(out, lse, ref_o, ref_l, f"rising d={d}")
+
+
+@pytest.mark.parametrize("heads", [(6, 2), (5, 1), (16, 2), (32, 2)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_group_sizes(heads, d):
+    """Query heads per KV head of 3 and 5 (a 16-row-head tile then ends inside
+    a row's group of heads), 8 and 16 (12 rows already give 96 and 192
+    row-heads per KV head), at two head sizes and every launch choice."""
+    hq, hkv = heads
+    wl = Workload(f"g{hq}x{hkv}", 83 + hq, 1, 3, hq, hkv, d, 8, 4, [170, 33], 0.88, grid_rows(4, 3),
+                  heavy_frac=0.02)
+    run_case(wl)
