@@ -341,3 +341,30 @@ def test_group_sizes(heads, d):
     wl = Workload(f"g{hq}x{hkv}", 83 + hq, 1, 3, hq, hkv, d, 8, 4, [170, 33], 0.88, grid_rows(4, 3),
                   heavy_frac=0.02)
     run_case(wl)
+
+
+@pytest.mark.parametrize("d", [96, 128])
+def test_layers_with_different_lengths(d):
+    """Three layers: the prefix on every layer, then accepted tokens on the
+    middle layer only (evicting window positions there), so the layers'
+    lengths differ.  Storage bit-exact against the oracle; every layer's call
+    against the oracle's (each layer has its own data, lengths and sections)."""
+    H = _h()
+    wl = Workload(f"layers{d}", 84, 3, 4, 4, 2, d, 8, 4, [150, 40], 0.88, grid_rows(4, 4),
+                  heavy_frac=0.02, capacity=200)
+    cache = H.make_cache(wl)
+    H.load_prefix(cache, wl)
+    oc = oracle.prefix_cache(wl)
+    n_new = [6, 3]
+    arrs = step_arrays(wl, 1, wl.lens, n_new)
+    cache.append(1, n_new, *[H.to_dev(a) for a in arrs])
+    assert oc.append(1, n_new, *arrs) == oracle.ORA_OK
+    torch.cuda.synchronize()
+    assert [cache.lengths(k) for k in range(3)] == [[150, 40], [156, 43], [150, 40]]
+    assert np.array_equal(cache.storage.cpu().numpy(), oc.image), "layout differs from the oracle"
+    for layer in range(3):
+        q, bk, bv = H.verify_inputs(wl, layer)
+        out, lse = cache.verify(layer, wl.rows, q, bk, bv, wl.n_blk)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oc.verify(layer, wl.rows, wl.queries(layer), *wl.block(layer), wl.n_blk)
+        assert_close(out, lse, ref_o, ref_l, f"layers d={d} layer={layer}")
