@@ -21,12 +21,12 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "self_speculative_verify_amd", "csrc")
-HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+HIPCC = os.environ.get("HIPCC") or (
+    "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc"))
 LDS_BYTES = 160 * 1024
 PRIVATE_MAX = 128            # bytes per lane
 
-pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None,
-                                reason="hipcc not available")
+pytestmark = pytest.mark.skipif(not HIPCC, reason="hipcc not available")
 
 LABEL = re.compile(r"^(\.LBB\d+_\d+|; %bb\.\d+):(.*)$")
 
