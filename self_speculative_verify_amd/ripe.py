@@ -121,7 +121,9 @@ def _check(status: int, what: str) -> None:
 
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
-        stream = torch.cuda.current_stream()
+        # the current device's current stream, read as a raw handle (no
+        # Stream object is built on every call)
+        return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(torch.cuda.current_device()))
     if isinstance(stream, torch.cuda.Stream):
         return ctypes.c_void_p(stream.cuda_stream)
     return ctypes.c_void_p(int(stream))
@@ -141,16 +143,25 @@ def config(n_layers, n_loops, n_heads_q, n_heads_kv, head_dim, window, batch, ca
                       capacity, max_block, anchor)
 
 
+_VIEW_TYPES = (torch.bfloat16, torch.int16, torch.uint16)
+_VIEW_DIMS = {}      # dims string -> positions of b, p, h, t in it (-1: absent)
+
+
 def kv_view(t: torch.Tensor, dims: str) -> RipeKVView:
     """A view of a bf16 tensor whose dimensions are named by ``dims``, a string
     over b (sequence), p (plane), h (KV head), t (token) ending in d (head
     dimension, stride 1).  Missing letters get stride 0."""
-    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+    if t.dtype not in _VIEW_TYPES:
         raise TypeError(f"expected a bfloat16 tensor, got {t.dtype}")
-    if t.dim() != len(dims) or not dims.endswith("d") or t.stride(-1) != 1:
+    st = t.stride()
+    if len(st) != len(dims) or not dims.endswith("d") or st[-1] != 1:
         raise ValueError(f"tensor of shape {tuple(t.shape)} does not match '{dims}' with d contiguous")
-    st = {c: t.stride(i) for i, c in enumerate(dims)}
-    return RipeKVView(t.data_ptr(), st.get("b", 0), st.get("p", 0), st.get("h", 0), st.get("t", 0))
+    pos = _VIEW_DIMS.get(dims)
+    if pos is None:
+        pos = _VIEW_DIMS[dims] = tuple(dims.find(c) for c in "bpht")
+    b, p, h, k = pos
+    return RipeKVView(t.data_ptr(), st[b] if b >= 0 else 0, st[p] if p >= 0 else 0,
+                      st[h] if h >= 0 else 0, st[k] if k >= 0 else 0)
 
 
 def null_view() -> RipeKVView:
