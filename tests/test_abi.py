@@ -84,3 +84,44 @@ def test_status_strings():
     for s in range(4):
         assert ripe.ripe_status_string(s)
     assert "capacity" in ripe.ripe_status_string(ripe.RIPE_ECAPACITY)
+
+
+# ---------------------------------------------------------------- binding views
+
+def test_kv_view_strides_by_name():
+    """kv_view maps each named dimension to its element stride; letters the
+    string leaves out get stride 0; views of two layouts in turn stay apart."""
+    import torch
+    from self_speculative_verify_amd import ripe
+    t5 = torch.zeros(2, 3, 4, 5, 64, dtype=torch.bfloat16)
+    v = ripe.kv_view(t5, "bphtd")
+    assert (v.s_b, v.s_plane, v.s_head, v.s_tok) == t5.stride()[:4]
+    assert v.ptr == t5.data_ptr()
+    t4 = torch.zeros(2, 6, 9, 32, dtype=torch.bfloat16)[:, :, 1:8]      # strided token dimension
+    w = ripe.kv_view(t4, "bhtd")
+    assert (w.s_b, w.s_plane, w.s_head, w.s_tok) == (t4.stride(0), 0, t4.stride(1), t4.stride(2))
+    assert w.ptr == t4.data_ptr()
+    t3 = torch.zeros(4, 7, 16, dtype=torch.bfloat16)
+    x = ripe.kv_view(t3, "ptd")
+    assert (x.s_b, x.s_plane, x.s_head, x.s_tok) == (0, t3.stride(0), 0, t3.stride(1))
+    v2 = ripe.kv_view(t5, "bphtd")                                      # again, after other strings
+    assert (v2.s_b, v2.s_plane, v2.s_head, v2.s_tok) == t5.stride()[:4]
+
+
+def test_kv_view_rejects_bad_tensors():
+    import torch
+    from self_speculative_verify_amd import ripe
+    with pytest.raises(TypeError):
+        ripe.kv_view(torch.zeros(2, 64), "td")                          # not 16-bit
+    with pytest.raises(ValueError):
+        ripe.kv_view(torch.zeros(64, 2, dtype=torch.bfloat16).t(), "td")  # d not contiguous
+    with pytest.raises(ValueError):
+        ripe.kv_view(torch.zeros(2, 64, dtype=torch.bfloat16), "htd")   # rank differs
+    with pytest.raises(ValueError):
+        ripe.kv_view(torch.zeros(2, 64, dtype=torch.bfloat16), "dt")    # does not end in d
+
+
+def test_stream_handle_passthrough():
+    """A raw stream handle given as an integer goes through unchanged."""
+    from self_speculative_verify_amd import ripe
+    assert ripe._stream(0x1234).value == 0x1234
